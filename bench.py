@@ -1,0 +1,292 @@
+"""Benchmark of the Prox sparse SwiGLU FFN forward on one MI355X.
+
+Default workload: one 8B-like FFN layer (d_model 4096, d_ff 14336, bf16
+weights N(0, 0.02^2)), one decode token, input keep 0.5, FFN sparsity 0.7,
+int8 per-row proxy.  A step is one full forward of the layer (both stages,
+five kernels).  Four copies of the weights and proxy (1.9 GB) are cycled so
+each step streams its weights from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line: µs per layer (back-to-back steps on one stream), the
+layer's effective GB/s against the 8 TB/s HBM peak, the dominant kernel's
+roofline (measured live with HIP events around each kernel), the HIP-graph
+variant, and the CPU oracle timed on the host as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama8b] [--batch 1]
+                    [--sparsity 0.7] [--mode int8_row] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "µs/FFN layer + HBM GB/s (% roofline), 4096×14336 bf16 @70% sparsity, B=1"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama8b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--sparsity", type=float, default=None)
+    ap.add_argument("--keep", type=float, default=None)
+    ap.add_argument("--mode", default=None)
+    ap.add_argument("--sets", type=int, default=4, help="weight copies cycled to defeat the Infinity Cache")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def kept_union(x_f32: np.ndarray, k_in: int) -> int:
+    """Number of input columns some token keeps (largest |x|, ties to the lower index)."""
+    keep = np.zeros(x_f32.shape[1], bool)
+    for row in x_f32:
+        order = np.lexsort((np.arange(row.size), -np.abs(row.astype(np.float64))))
+        keep[order[:k_in]] = True
+    return int(keep.sum())
+
+
+def algorithmic_bytes(d, F, B, k, k_union, bw, mode):
+    """Bytes the method must move for one layer (SURVEY-style accounting):
+    x, proxy codes of the kept columns, proxy scales, the selected gate/up/down
+    rows, the mask, the output."""
+    if mode == "int8_row":
+        proxy = 2 * k_union * F
+        scales = 2 * F * 4
+    else:
+        proxy = k_union * F  # two nibbles per byte, gate and up
+        scales = (d // 128) * 2 * F * 4
+    return dict(x=B * d * bw, proxy=proxy, scales=scales, gateup=2 * k * d * bw, down=k * d * bw,
+                sel=k * 4, out=B * d * bw)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "free_sparse_swiglu_stage1_amd", "csrc"))):
+        with open(os.path.join(ROOT, "free_sparse_swiglu_stage1_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_digest") != source_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import free_sparse_swiglu_stage1_amd as P
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    P.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    d, F, dtype = wl.d, wl.F, wl.dtype
+    B = args.batch
+    if args.sparsity is not None:
+        sp = args.sparsity
+    else:
+        sp = 0.7 if 0.7 in wl.sparsities else wl.sparsities[0]
+    keep = wl.input_keep if args.keep is None else args.keep
+    mode = wl.mode if args.mode is None else args.mode
+    bw = 4 if dtype == "f32" else 2
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    wg, wu, wd = synth.make_weights(d, F, wl.std, dtype, seed=0, layer=0)
+    x_host = synth.make_x(B, d, dtype, seed=0)
+    w0 = P.pack_weights(to_dev(wg), to_dev(wu), to_dev(wd))
+    p0 = P.quantize_proxy(w0, mode)
+    sets = [(w0, p0)]
+    for _ in range(1, args.sets):
+        w = P.Weights(w0.w_gu.clone(), w0.w_down_t.clone(), d, F)
+        p = P.Proxy(p0.codes.clone(), p0.scales.clone(), p0.mode, d, F)
+        sets.append((w, p))
+    x = to_dev(x_host)
+    out = torch.empty_like(x)
+    ws = P.alloc_workspace(d, F, B, mode, dev)
+    torch.cuda.synchronize()
+    print("setup %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
+
+    k_in, k = P.counts(d, F, keep, sp)
+    k_union = kept_union(synth.to_f32(x_host), k_in)
+    parts = algorithmic_bytes(d, F, B, k, k_union, bw, mode)
+    layer_bytes = sum(parts.values())
+    R = len(sets)
+
+    def step(i):
+        w, p = sets[i % R]
+        P.ffn_forward(x, w, p, keep, sp, out=out, workspace=ws)
+
+    # ---- eager, back to back on one stream
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    us_layer = 1000.0 * ms_total / args.steps
+    print("eager %.2f us/layer" % us_layer, file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations, HIP events recorded between the kernels
+    n_t = min(args.steps, 200)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_t)]
+    for i in range(n_t):
+        w, p = sets[i % R]
+        P.ffn_forward_timed(x, w, p, keep, sp, evs[i], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    per = {name: [] for name in P.STEP_NAMES}
+    lat = []
+    for row in evs[n_t // 10:]:
+        for j, name in enumerate(P.STEP_NAMES):
+            per[name].append(1000.0 * row[j].elapsed_time(row[j + 1]))
+        lat.append(1000.0 * row[0].elapsed_time(row[5]))
+    kern_us = {n: statistics.mean(v) for n, v in per.items()}
+    kern_bytes = {"xselect": parts["x"], "proxy": parts["proxy"] + parts["scales"], "topk": F * 4 + k * 4,
+                  "gateup": parts["gateup"] + parts["x"] + 4 * B * k, "down": parts["down"] + parts["out"] + 4 * B * k}
+    lat.sort()
+    latency = dict(median=lat[len(lat) // 2], p10=lat[len(lat) // 10], p90=lat[(9 * len(lat)) // 10])
+
+    # ---- HIP graph of R forwards (one per weight set), replayed
+    graph_us = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for r in range(R):
+                        step(r)
+            torch.cuda.synchronize()
+            ref = out.clone()
+            for _ in range(max(1, args.warmup // R)):
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            n_rep = max(1, args.steps // R)
+            for _ in range(n_rep):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_us = 1000.0 * e0.elapsed_time(e1) / (n_rep * R)
+            step(R - 1)
+            torch.cuda.synchronize()
+            if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+                graph_us = None
+                print("graph replay output differs from eager; graph timing dropped", file=sys.stderr)
+        except Exception as exc:  # pragma: no cover
+            print("graph capture unavailable: %r" % (exc,), file=sys.stderr)
+    print("graph %s us/layer" % graph_us, file=sys.stderr, flush=True)
+
+    dom = "gateup"
+    dom_bytes = parts["gateup"]
+    dom_gbps = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profiles(dom, args.workload)
+    roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern_us[dom], 3)}
+    layer_gbps = layer_bytes / (us_layer * 1e-6) / 1e9
+
+    # ---- CPU oracle baseline (bounded sample on the host cores)
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        oracle.build(force=False)
+        proxy_q = oracle.quantize(wg, mode) + oracle.quantize(wu, mode)
+        times = []
+        deadline = time.time() + 12.0
+        while True:
+            t = time.perf_counter()
+            ref = oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode)
+            times.append(time.perf_counter() - t)
+            if time.time() > deadline or len(times) >= 40:
+                break
+        cpu = {"value": round(1e6 * statistics.median(times), 1), "unit": "us/layer",
+               "cores": oracle.get_threads(), "kind": "oracle",
+               "sample": "%d full oracle forwards of the same layer and token (median), binary64 C loops"
+                         % len(times)}
+        # parity of the timed configuration against the oracle
+        sel = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
+        y = P.ffn_forward(x, w0, p0, keep, sp, sel_out=sel)
+        torch.cuda.synchronize()
+        sel_np = sel[:k].cpu().numpy().astype(np.int64)
+        ok, msg = oracle.mask_admissible(sel_np, ref["sel"], ref["score"], ref["T"], k)
+        y_ref, _ = oracle.ffn_masked(x_host, wg, wu, wd, sel_np)
+        yg = (y.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else y.cpu().numpy())
+        yg = oracle.as_f64(yg)
+        err = max(float(np.abs(yg[b] - y_ref[b]).max() / np.abs(y_ref[b]).max()) for b in range(B))
+        parity = {"mask_admissible": bool(ok), "max_rel_err": err, "mask": msg}
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s" % (args.workload, d, F, dtype, B, sp, keep, mode),
+                   "d_model": d, "d_ff": F, "batch": B, "ffn_sparsity": sp, "input_keep": keep, "proxy": mode,
+                   "k": k, "k_in": k_in, "kept_union": k_union, "weight_sets": R},
+        "layer_bytes": layer_bytes,
+        "layer_gbps": round(layer_gbps, 1),
+        "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
+        "latency_us": {kk: round(v, 2) for kk, v in latency.items()},
+        "graph_us_per_layer": None if graph_us is None else round(graph_us, 3),
+        "kernels_us": {kk: round(v, 3) for kk, v in kern_us.items()},
+        "kernels_gbps": {kk: round(kern_bytes[kk] / (kern_us[kk] * 1e-6) / 1e9, 1) for kk in kern_us},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,442 @@
+// C ABI of the Prox library: argument validation, counts, workspace layout
+// and the launch sequence of the two stages.  See include/prox.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/prox.h"
+#include "kernels.h"
+
+using namespace prox;
+
+namespace {
+
+constexpr int kMaxBatch = 16;
+constexpr int kMaxBatchInt4 = 4;
+constexpr int kCounters = 1024;          // [0,512): proxy channel blocks, [512,1024): down slices
+constexpr int kTargetProxyBlocks = 1024;
+constexpr int kTargetDownBlocks = 512;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool bad_ptr(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) != 0; }
+bool bad_ptr_opt(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
+
+int elem_bytes(prox_dtype t) { return t == PROX_F32 ? 4 : 2; }
+
+prox_status check_shape(int64_t d, int64_t F)
+{
+    if (d < 8 || d > 16384 || F < 16 || F > 65536) return PROX_ERR_UNSUPPORTED;
+    if (d % 8 != 0 || F % 16 != 0) return PROX_ERR_UNSUPPORTED;
+    return PROX_OK;
+}
+
+prox_status check_mode_shape(int64_t d, int64_t F, int mode)
+{
+    prox_status s = check_shape(d, F);
+    if (s != PROX_OK) return s;
+    if (mode != PROX_Q_INT8_ROW && mode != PROX_Q_INT4_G128) return PROX_ERR_UNSUPPORTED;
+    if (mode == PROX_Q_INT4_G128 && d % 128 != 0) return PROX_ERR_UNSUPPORTED;
+    return PROX_OK;
+}
+
+prox_status check_weights(const prox_weights *w)
+{
+    if (!w) return PROX_ERR_INVALID_ARG;
+    if (w->dtype != PROX_F32 && w->dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    prox_status s = check_shape(w->d_model, w->d_ff);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(w->w_gu) || bad_ptr(w->w_down_t)) return PROX_ERR_INVALID_ARG;
+    return PROX_OK;
+}
+
+prox_status check_proxy(const prox_proxy *p, const prox_weights *w)
+{
+    if (!p) return PROX_ERR_INVALID_ARG;
+    if (p->d_model != w->d_model || p->d_ff != w->d_ff) return PROX_ERR_INVALID_ARG;
+    prox_status s = check_mode_shape(p->d_model, p->d_ff, p->mode);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(p->codes) || bad_ptr(p->scales)) return PROX_ERR_INVALID_ARG;
+    return PROX_OK;
+}
+
+prox_status check_batch(int64_t B, int mode)
+{
+    if (B < 1) return PROX_ERR_INVALID_ARG;
+    if (B > kMaxBatch) return PROX_ERR_UNSUPPORTED;
+    if (mode == PROX_Q_INT4_G128 && B > kMaxBatchInt4) return PROX_ERR_UNSUPPORTED;
+    return PROX_OK;
+}
+
+prox_status counts(int64_t d, int64_t F, float keep, float sp, int64_t *k_in, int64_t *k)
+{
+    if (isnan(keep) || !(keep > 0.0f) || keep > 1.0f) return PROX_ERR_INVALID_ARG;
+    if (isnan(sp) || sp < 0.0f || sp > 1.0f) return PROX_ERR_INVALID_ARG;
+    double a = floor((double)keep * (double)d + 0.5);
+    if (a < 1.0) a = 1.0;
+    if (a > (double)d) a = (double)d;
+    double b = floor((1.0 - (double)sp) * (double)F + 0.5);
+    if (b < 0.0) b = 0.0;
+    if (b > (double)F) b = (double)F;
+    *k_in = (int64_t)a;
+    *k = (int64_t)b;
+    return PROX_OK;
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+ProxyPlan proxy_plan(int64_t d, int64_t F, int64_t B, int mode)
+{
+    ProxyPlan p;
+    p.qbits = mode == PROX_Q_INT4_G128 ? 4 : 8;
+    if (p.qbits == 8) {
+        p.cpl = 4;
+        p.nb = B == 1 ? 1 : (B <= 4 ? 4 : 16);
+    } else {
+        p.cpl = 8;
+        p.nb = B == 1 ? 1 : 4;
+    }
+    p.n_cblocks = ceil_div(F, 64 * p.cpl);
+    const int gran = p.qbits == 4 ? 128 : 32;
+    const int s_min = ceil_div(d, kMaxSplitRange);
+    int s = ceil_div(kTargetProxyBlocks, p.n_cblocks);
+    const int s_max = ceil_div(d, 128);
+    if (s > s_max) s = s_max;
+    if (s < s_min) s = s_min;
+    int R = ceil_div(ceil_div(d, s), gran) * gran;
+    if (R > kMaxSplitRange) R = kMaxSplitRange;
+    p.R = R;
+    p.S = ceil_div(d, R);
+    return p;
+}
+
+DownPlan down_plan(int64_t d, int64_t k, int64_t B, prox_dtype t)
+{
+    DownPlan p;
+    p.vec = 16 / elem_bytes(t);
+    p.cols = 64 * p.vec;
+    p.n_slices = ceil_div(d, p.cols);
+    int s = ceil_div(kTargetDownBlocks, p.n_slices);
+    const int s_k = (int)(k / 16);  // at least ~16 rows per split
+    if (k >= 0 && s > s_k) s = s_k;
+    if (s < 1) s = 1;
+    p.S = s;
+    p.nb = B >= 4 ? 4 : (int)B;
+    return p;
+}
+
+struct Workspace {
+    uint32_t *counters;
+    float *xh;
+    float *proxy_part;
+    float *score;
+    int32_t *sel;
+    float *s_sp;
+    float *down_part;
+    size_t bytes;
+};
+
+// Offsets depend only on (d, F, B, mode); the down partials are sized for the
+// largest split count any k can use (the bf16 slicing, which has fewer slices).
+Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
+{
+    const ProxyPlan pp = proxy_plan(d, F, B, mode);
+    const int down_s_max = ceil_div(kTargetDownBlocks, ceil_div(d, 64 * 8));
+    size_t off = 0;
+    Workspace w;
+    char *b = (char *)base;
+    auto take = [&](size_t n) { char *p = b ? b + off : nullptr; off += align256(n); return p; };
+    w.counters = (uint32_t *)take(sizeof(uint32_t) * kCounters);
+    w.xh = (float *)take(sizeof(float) * B * d);
+    w.proxy_part = (float *)take(sizeof(float) * (size_t)pp.S * B * 2 * F);
+    w.score = (float *)take(sizeof(float) * F);
+    w.sel = (int32_t *)take(sizeof(int32_t) * F);
+    w.s_sp = (float *)take(sizeof(float) * B * F);
+    w.down_part = (float *)take(sizeof(float) * (size_t)down_s_max * 4 * d);
+    w.bytes = off;
+    return w;
+}
+
+prox_status hip_status(hipError_t e) { return e == hipSuccess ? PROX_OK : PROX_ERR_HIP; }
+
+#define TRY_HIP(expr)                                           \
+    do {                                                        \
+        hipError_t e_ = (expr);                                 \
+        if (e_ != hipSuccess) return PROX_ERR_HIP;              \
+    } while (0)
+
+// Records ev[i] on the stream when timing events were supplied.
+hipError_t mark(hipEvent_t *ev, int i, hipStream_t st) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; }
+
+// Stage 1 into `sel` (k entries), scores into `score`.
+prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const prox_proxy *p, int64_t k_in,
+                       int64_t k, int32_t *sel, float *score, const Workspace &ws, hipStream_t st,
+                       hipEvent_t *ev = nullptr)
+{
+    const int64_t d = w->d_model, F = w->d_ff;
+    const ProxyPlan pp = proxy_plan(d, F, B, p->mode);
+    TRY_HIP(mark(ev, 0, st));
+    TRY_HIP(launch_xselect(w->dtype == PROX_F32 ? 0 : 1, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
+                           kCounters, st));
+    TRY_HIP(mark(ev, 1, st));
+    TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes, (const float *)p->scales,
+                         ws.proxy_part, score, ws.counters, st));
+    TRY_HIP(mark(ev, 2, st));
+    if (k > 0) TRY_HIP(launch_topk(score, (int)F, (int)k, sel, st));
+    return PROX_OK;
+}
+
+// Stage 2 on `sel` (nullptr = every channel).  Counters must be zero.
+prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const int32_t *sel, int64_t k,
+                       const void *residual, void *out, int32_t *iota_out, const Workspace &ws, hipStream_t st,
+                       hipEvent_t *ev = nullptr)
+{
+    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    const int64_t d = w->d_model;
+    TRY_HIP(mark(ev, 3, st));
+    if (k == 0) {
+        TRY_HIP(launch_fill_out(dt, (int)B, (int)d, residual, out, st));
+        TRY_HIP(mark(ev, 4, st));
+        return hip_status(mark(ev, 5, st));
+    }
+    TRY_HIP(launch_gateup(dt, x, (int)B, (int)d, w->w_gu, sel, (int)k, ws.s_sp, iota_out, st));
+    TRY_HIP(mark(ev, 4, st));
+    const DownPlan dp = down_plan(d, k, B, w->dtype);
+    TRY_HIP(launch_down(dt, dp, ws.s_sp, (int)B, (int)k, w->w_down_t, sel, (int)d, ws.down_part, residual, out,
+                        ws.counters + 512, st));
+    return hip_status(mark(ev, 5, st));
+}
+
+prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const prox_proxy *p, float keep,
+                         float sp, const void *residual, void *out, int32_t *sel_out, void *workspace,
+                         size_t ws_bytes, hipStream_t st, hipEvent_t *ev = nullptr)
+{
+    prox_status s = check_weights(w);
+    if (s != PROX_OK) return s;
+    s = check_proxy(p, w);
+    if (s != PROX_OK) return s;
+    s = check_batch(B, p->mode);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(x) || bad_ptr(out) || bad_ptr_opt(sel_out) || bad_ptr_opt(residual) || bad_ptr(workspace))
+        return PROX_ERR_INVALID_ARG;
+    if (x == out || x == residual) return PROX_ERR_INVALID_ARG;
+    int64_t k_in, k;
+    s = counts(w->d_model, w->d_ff, keep, sp, &k_in, &k);
+    if (s != PROX_OK) return s;
+    const Workspace ws = layout(w->d_model, w->d_ff, B, p->mode, workspace);
+    if (ws_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
+    const int64_t F = w->d_ff;
+    if (k == 0 || k == F) {  // no Stage 1
+        TRY_HIP(mark(ev, 0, st));
+        TRY_HIP(launch_zero_u32(ws.counters, kCounters, st));
+        TRY_HIP(mark(ev, 1, st));
+        TRY_HIP(mark(ev, 2, st));
+        return run_stage2(x, B, w, nullptr, k, residual, out, k ? sel_out : nullptr, ws, st, ev);
+    }
+    int32_t *sel = sel_out ? sel_out : ws.sel;
+    s = run_stage1(x, B, w, p, k_in, k, sel, ws.score, ws, st, ev);
+    if (s != PROX_OK) return s;
+    return run_stage2(x, B, w, sel, k, residual, out, nullptr, ws, st, ev);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *prox_status_string(int status)
+{
+    switch (status) {
+    case PROX_OK: return "PROX_OK";
+    case PROX_ERR_INVALID_ARG: return "PROX_ERR_INVALID_ARG: invalid argument";
+    case PROX_ERR_UNSUPPORTED: return "PROX_ERR_UNSUPPORTED: unsupported shape, dtype, mode or batch";
+    case PROX_ERR_WORKSPACE: return "PROX_ERR_WORKSPACE: workspace too small";
+    case PROX_ERR_HIP: return "PROX_ERR_HIP: HIP launch failed";
+    default: return "unknown prox status";
+    }
+}
+
+const char *prox_version(void) { return "prox-gfx950 0.1"; }
+
+prox_status prox_counts(int64_t d, int64_t F, float keep, float sp, int64_t *k_in, int64_t *k)
+{
+    if (!k_in || !k) return PROX_ERR_INVALID_ARG;
+    prox_status s = check_shape(d, F);
+    if (s != PROX_OK) return s;
+    return counts(d, F, keep, sp, k_in, k);
+}
+
+prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *w_down, int64_t d, int64_t F,
+                              prox_dtype dtype, void *w_gu_out, void *w_down_t_out, hipStream_t stream)
+{
+    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    prox_status s = check_shape(d, F);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(w_gate) || bad_ptr(w_up) || bad_ptr(w_down) || bad_ptr(w_gu_out) || bad_ptr(w_down_t_out))
+        return PROX_ERR_INVALID_ARG;
+    return hip_status(launch_pack(dtype == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F, w_gu_out,
+                                  w_down_t_out, stream));
+}
+
+prox_status prox_proxy_sizes(int64_t d, int64_t F, prox_qmode mode, size_t *codes_bytes, size_t *scales_bytes)
+{
+    if (!codes_bytes || !scales_bytes) return PROX_ERR_INVALID_ARG;
+    prox_status s = check_mode_shape(d, F, mode);
+    if (s != PROX_OK) return s;
+    if (mode == PROX_Q_INT8_ROW) {
+        *codes_bytes = (size_t)d * 2 * F;
+        *scales_bytes = sizeof(float) * 2 * F;
+    } else {
+        *codes_bytes = (size_t)d * F;
+        *scales_bytes = sizeof(float) * (d / 128) * 2 * F;
+    }
+    return PROX_OK;
+}
+
+prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *codes, void *scales,
+                                hipStream_t stream)
+{
+    prox_status s = check_weights(w);
+    if (s != PROX_OK) return s;
+    s = check_mode_shape(w->d_model, w->d_ff, mode);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(codes) || bad_ptr(scales)) return PROX_ERR_INVALID_ARG;
+    return hip_status(launch_quantize(w->dtype == PROX_F32 ? 0 : 1, mode == PROX_Q_INT4_G128 ? 4 : 8, w->w_gu,
+                                      (int)w->d_model, (int)w->d_ff, (uint8_t *)codes, (float *)scales, stream));
+}
+
+prox_status prox_workspace_size(int64_t d, int64_t F, int64_t B, prox_qmode mode, size_t *bytes)
+{
+    if (!bytes) return PROX_ERR_INVALID_ARG;
+    prox_status s = check_mode_shape(d, F, mode);
+    if (s != PROX_OK) return s;
+    s = check_batch(B, mode);
+    if (s != PROX_OK) return s;
+    *bytes = layout(d, F, B, mode, nullptr).bytes;
+    return PROX_OK;
+}
+
+prox_status prox_ffn_forward(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                             float input_keep, float ffn_sparsity, void *out, int32_t *sel_idx_out,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, nullptr, out, sel_idx_out, workspace,
+                        workspace_bytes, stream);
+}
+
+prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                                      float input_keep, float ffn_sparsity, const void *residual, void *out,
+                                      int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream)
+{
+    if (bad_ptr(residual)) return PROX_ERR_INVALID_ARG;
+    return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, residual, out, sel_idx_out, workspace,
+                        workspace_bytes, stream);
+}
+
+prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                                   float input_keep, float ffn_sparsity, void *out, int32_t *sel_idx_out,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events)
+{
+    if (!events) return PROX_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+        if (!events[i]) return PROX_ERR_INVALID_ARG;
+    return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, nullptr, out, sel_idx_out, workspace,
+                        workspace_bytes, stream, events);
+}
+
+prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                               float input_keep, float ffn_sparsity, int32_t *sel_idx_out, float *scores_out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    prox_status s = check_weights(w);
+    if (s != PROX_OK) return s;
+    s = check_proxy(p, w);
+    if (s != PROX_OK) return s;
+    s = check_batch(batch, p->mode);
+    if (s != PROX_OK) return s;
+    if (bad_ptr(x) || bad_ptr(sel_idx_out) || bad_ptr_opt(scores_out) || bad_ptr(workspace))
+        return PROX_ERR_INVALID_ARG;
+    int64_t k_in, k;
+    s = counts(w->d_model, w->d_ff, input_keep, ffn_sparsity, &k_in, &k);
+    if (s != PROX_OK) return s;
+    if (k == w->d_ff) return PROX_ERR_INVALID_ARG;
+    const Workspace ws = layout(w->d_model, w->d_ff, batch, p->mode, workspace);
+    if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
+    return run_stage1(x, batch, w, p, k_in, k, sel_idx_out, scores_out ? scores_out : ws.score, ws, stream);
+}
+
+prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_idx_out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (n < 1 || n > 65536 || k < 0 || k > n) return PROX_ERR_INVALID_ARG;
+    if (bad_ptr(scores) || bad_ptr(sel_idx_out)) return PROX_ERR_INVALID_ARG;
+    if (k == 0) return PROX_OK;
+    return hip_status(launch_topk(scores, (int)n, (int)k, sel_idx_out, stream));
+}
+
+prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *w, const int32_t *sel_idx,
+                              int64_t k, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    prox_status s = check_weights(w);
+    if (s != PROX_OK) return s;
+    s = check_batch(batch, PROX_Q_INT8_ROW);
+    if (s != PROX_OK) return s;
+    if (k < 0 || k > w->d_ff) return PROX_ERR_INVALID_ARG;
+    if (bad_ptr(x) || bad_ptr(out) || bad_ptr(workspace) || (k > 0 && bad_ptr(sel_idx))) return PROX_ERR_INVALID_ARG;
+    if (x == out) return PROX_ERR_INVALID_ARG;
+    const Workspace ws = layout(w->d_model, w->d_ff, batch, PROX_Q_INT8_ROW, workspace);
+    if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
+    TRY_HIP(launch_zero_u32(ws.counters, kCounters, stream));
+    return run_stage2(x, batch, w, sel_idx, k, nullptr, out, nullptr, ws, stream);
+}
+
+prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d, prox_dtype dtype, float eps, void *out,
+                         hipStream_t stream)
+{
+    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    if (batch < 1 || batch > 4096 || d < 1 || d > 65536 || isnan(eps) || eps < 0.0f) return PROX_ERR_INVALID_ARG;
+    if (bad_ptr(h) || bad_ptr(out)) return PROX_ERR_INVALID_ARG;
+    return hip_status(launch_rmsnorm(dtype == PROX_F32 ? 0 : 1, h, (int)batch, (int)d, eps, out, stream));
+}
+
+prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layers, const prox_proxy *proxies,
+                               int64_t n_layers, float eps, float input_keep, float ffn_sparsity, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    if (!layers || !proxies || n_layers < 1) return PROX_ERR_INVALID_ARG;
+    if (isnan(eps) || eps < 0.0f) return PROX_ERR_INVALID_ARG;
+    if (bad_ptr(h) || bad_ptr(workspace)) return PROX_ERR_INVALID_ARG;
+    const prox_weights &w0 = layers[0];
+    for (int64_t l = 0; l < n_layers; ++l) {
+        prox_status s = check_weights(&layers[l]);
+        if (s != PROX_OK) return s;
+        s = check_proxy(&proxies[l], &layers[l]);
+        if (s != PROX_OK) return s;
+        if (layers[l].d_model != w0.d_model || layers[l].d_ff != w0.d_ff || layers[l].dtype != w0.dtype ||
+            proxies[l].mode != proxies[0].mode)
+            return PROX_ERR_INVALID_ARG;
+    }
+    prox_status s = check_batch(batch, proxies[0].mode);
+    if (s != PROX_OK) return s;
+    int64_t k_in, k;
+    s = counts(w0.d_model, w0.d_ff, input_keep, ffn_sparsity, &k_in, &k);
+    if (s != PROX_OK) return s;
+    size_t ffn_bytes = 0;
+    s = prox_workspace_size(w0.d_model, w0.d_ff, batch, proxies[0].mode, &ffn_bytes);
+    if (s != PROX_OK) return s;
+    const size_t need = ffn_bytes + 256 + (size_t)batch * w0.d_model * 4;
+    if (workspace_bytes < need) return PROX_ERR_WORKSPACE;
+    void *xn = (char *)workspace + align256(ffn_bytes);
+    for (int64_t l = 0; l < n_layers; ++l) {
+        TRY_HIP(launch_rmsnorm(w0.dtype == PROX_F32 ? 0 : 1, h, (int)batch, (int)w0.d_model, eps, xn, stream));
+        s = forward_impl(xn, batch, &layers[l], &proxies[l], input_keep, ffn_sparsity, h, h, nullptr, workspace,
+                         ffn_bytes, stream);
+        if (s != PROX_OK) return s;
+    }
+    return PROX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prox {
+
+// Longest input range one proxy workgroup compacts in LDS.
+constexpr int kMaxSplitRange = 512;
+
+// Launch shape of the proxy GEMV (K1).
+struct ProxyPlan {
+    int qbits;      // 8 or 4
+    int cpl;        // channels per lane
+    int nb;         // tokens held in registers (>= batch)
+    int n_cblocks;  // ceil(F / (64 * cpl))
+    int R;          // inputs per split (multiple of 128 for int4)
+    int S;          // number of input splits
+};
+
+// Launch shape of the down projection (K4).
+struct DownPlan {
+    int vec;        // columns per lane (16-byte loads)
+    int cols;       // columns per workgroup slice = 64 * vec
+    int n_slices;   // ceil(d / cols)
+    int S;          // channel-rank splits
+    int nb;         // tokens per pass
+};
+
+hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
+                          int n_counters, hipStream_t st);
+hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
+                        const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st);
+hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st);
+
+hipError_t launch_gateup(int dtype, const void *x, int B, int d, const void *w_gu, const int32_t *sel, int k,
+                         float *s_sp, int32_t *iota_out, hipStream_t st);
+hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
+                       const int32_t *sel, int d, float *part, const void *residual, void *out,
+                       uint32_t *counters, hipStream_t st);
+hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+
+hipError_t launch_pack(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,
+                       void *w_gu, void *w_down_t, hipStream_t st);
+hipError_t launch_quantize(int dtype, int qbits, const void *w_gu, int d, int F, uint8_t *codes, float *scales,
+                           hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, const void *h, int B, int d, float eps, void *out, hipStream_t st);
+
+}  // namespace prox

@@ -1,0 +1,214 @@
+/*
+ * prox.h -- C ABI of the MI355X (gfx950) Prox sparse SwiGLU FFN library.
+ *
+ * Prox ("Prox: Training-Free FFN Activation Sparsity via Approximate
+ * Intermediate-Channel Salience in LLMs") runs a SwiGLU FFN
+ *     y = W_down (silu(W_gate x) * (W_up x))
+ * in two stages (technical summary, "Methodology: The Prox Framework"):
+ *   Stage 1 (Lightweight Proxy Construction): sparsify x by magnitude, run it
+ *     through quantized proxy copies of W_gate and W_up, score every
+ *     intermediate channel by |silu(g~) * u~| and keep the top k channels as
+ *     one mask shared by all three projections;
+ *   Stage 2 (Exact Sparse Computation): compute gate, up, SiLU-multiply and
+ *     down exactly, with the original weights, on the selected channels only.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" point to device memory (any allocator); the
+ *    library never allocates or frees device memory and keeps no state
+ *    between calls.  Host pointers are read or written before return.
+ *  - Work is enqueued on the caller's HIP stream and runs asynchronously; no
+ *    call synchronizes.  Results are bitwise deterministic run to run.
+ *  - Argument errors are reported before anything is enqueued, with nothing
+ *    written.  A failed launch returns PROX_ERR_HIP.  No call aborts and no
+ *    C++ exception crosses this interface.
+ *  - Device pointers must be 16-byte aligned.  x and out must not alias.
+ *  - Shapes: d_model % 8 == 0 (int4-g128 proxy: % 128), d_ff % 16 == 0,
+ *    8 <= d_model <= 16384, 16 <= d_ff <= 65536, 1 <= batch <= 16
+ *    (int4-g128 proxy: batch <= 4); other sizes return PROX_ERR_UNSUPPORTED.
+ *  - One workspace must not be used by two calls that may run concurrently.
+ *    Its contents need no initialization and mean nothing between calls.
+ *
+ * Notation: d = d_model, F = d_ff, B = batch, bf16 = bfloat16 bit patterns.
+ */
+#ifndef PROX_H
+#define PROX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PROX_OK = 0,
+    PROX_ERR_INVALID_ARG = -1, /* null/misaligned pointer, NaN or out-of-range fraction, bad batch */
+    PROX_ERR_UNSUPPORTED = -2, /* shape, dtype or mode outside the supported set above */
+    PROX_ERR_WORKSPACE = -3,   /* workspace_bytes smaller than prox_workspace_size() */
+    PROX_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+} prox_status;
+
+/* Element type of x, out and the full-precision weights (one type per call).
+ * Accumulation is always fp32. */
+typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
+
+/* Proxy weight format.  The pages specify INT4 proxies without a scheme;
+ * both formats are symmetric absmax with fp32 scales and round-to-nearest-
+ * even codes:  INT8_ROW = one scale per output channel, codes in [-127,127];
+ * INT4_G128 = one scale per (channel, 128 consecutive inputs), codes in
+ * [-7,7]. */
+typedef enum { PROX_Q_INT8_ROW = 0, PROX_Q_INT4_G128 = 1 } prox_qmode;
+
+/* Full-precision weights in the library's channel-major layout (produced by
+ * prox_pack_weights):
+ *   w_gu     [F][2][d]  row j*2 = gate row j, row j*2+1 = up row j, so the two
+ *                       rows a selected channel needs are one contiguous run;
+ *   w_down_t [F][d]     = W_down^T: row j holds the d outputs channel j feeds. */
+typedef struct {
+    int64_t d_model, d_ff;
+    prox_dtype dtype;
+    const void *w_gu;     /* device */
+    const void *w_down_t; /* device */
+} prox_weights;
+
+/* Quantized proxy of W_gate and W_up (produced by prox_quantize_proxy).
+ * Layout, input-major so that a skipped input is a skipped contiguous run:
+ *   INT8_ROW:  codes  int8  [d][2][F]        codes[i][0][j] = q_gate[j][i],
+ *                                            codes[i][1][j] = q_up[j][i]
+ *              scales fp32  [2][F]
+ *   INT4_G128: codes  uint8 [d][2][F/2]      byte p of half h of input row i holds
+ *                                            channel 2p in bits 0..3 and 2p+1 in
+ *                                            bits 4..7, each as (q + 8) in [1,15]
+ *              scales fp32  [d/128][2][F]    scales[g][h][j] for inputs g*128..+127
+ * Dequantized proxy weight = scale * q. */
+typedef struct {
+    prox_qmode mode;
+    int64_t d_model, d_ff;
+    const void *codes;  /* device */
+    const void *scales; /* device */
+} prox_proxy;
+
+/* Human-readable name of a status code (static string). */
+const char *prox_status_string(int status);
+
+/* Library version string, e.g. "prox-gfx950 0.1". */
+const char *prox_version(void);
+
+/* Counts of kept inputs per token and kept channels, as the library computes
+ * them (Sparsity Allocation: input sparsity keeps a fraction of input entries,
+ * Stage-2 sparsity drops a fraction of intermediate channels):
+ *   k_in = clamp(floor(input_keep * d + 1/2), 1, d)
+ *   k    = clamp(floor((1 - ffn_sparsity) * F + 1/2), 0, F)
+ * evaluated in binary64 on the binary32 arguments.  input_keep in (0,1],
+ * ffn_sparsity in [0,1], both not NaN, else PROX_ERR_INVALID_ARG.  Host-only. */
+prox_status prox_counts(int64_t d_model, int64_t d_ff, float input_keep, float ffn_sparsity,
+                        int64_t *k_in, int64_t *k);
+
+/* Offline: repack nn.Linear weights into the channel-major layout above.
+ *   w_gate, w_up [F][d], w_down [d][F] (device, row-major, dtype)
+ *   w_gu_out [F][2][d], w_down_t_out [F][d] (device, dtype; caller-allocated)
+ * Inputs and outputs must not overlap. */
+prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *w_down,
+                              int64_t d_model, int64_t d_ff, prox_dtype dtype,
+                              void *w_gu_out, void *w_down_t_out, hipStream_t stream);
+
+/* Bytes of the proxy buffers for a shape and mode (host-only). */
+prox_status prox_proxy_sizes(int64_t d_model, int64_t d_ff, prox_qmode mode,
+                             size_t *codes_bytes, size_t *scales_bytes);
+
+/* Offline: quantize the proxy of W_gate and W_up from packed weights
+ * (Stage 1, "Input Sparsity & Quantization": quantized proxy copies of the up
+ * and gate projections).  Per segment (a channel's row for INT8_ROW, a
+ * channel's 128-input group for INT4_G128): a = max |w| (binary32),
+ * scale = a / qmax rounded to binary32, q = clamp(rint(w / scale)) with
+ * round-to-nearest-even binary32 division; a == 0 gives scale 0 and q 0.
+ * codes, scales: device buffers of prox_proxy_sizes() bytes. */
+prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *codes, void *scales,
+                                hipStream_t stream);
+
+/* Workspace bytes a forward call with these sizes needs (host-only). */
+prox_status prox_workspace_size(int64_t d_model, int64_t d_ff, int64_t batch, prox_qmode mode,
+                                size_t *bytes);
+
+/* The Prox FFN forward (both stages).
+ *   x   [B][d] device, w->dtype: the FFN input (already normalized).
+ *   out [B][d] device, w->dtype: y = sum over selected j of W_down[:, j] *
+ *       silu(W_gate[j] . x) * (W_up[j] . x), fp32 accumulation, rounded to
+ *       nearest-even on store.
+ *   sel_idx_out: nullable device int32 [k]; receives the mask as ascending
+ *       channel indices.
+ * Stage 1 keeps, per token, the k_in largest |x_i| (ties: lower i), scores
+ * channel j by score_j = sum_b |silu(g~_bj) * u~_bj| with the proxy
+ * projections of the sparsified x, and selects the k largest scores (ties:
+ * lower j) as one mask for the whole batch.  Stage 2 uses the dense x.
+ * k == F skips Stage 1 (every channel is selected); k == 0 writes zeros. */
+prox_status prox_ffn_forward(const void *x, int64_t batch, const prox_weights *w,
+                             const prox_proxy *p, float input_keep, float ffn_sparsity, void *out,
+                             int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* As prox_ffn_forward, then out = residual + y (the add in fp32, one rounding).
+ * residual [B][d] device, may alias out (in-place residual update) but not x. */
+prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_weights *w,
+                                      const prox_proxy *p, float input_keep, float ffn_sparsity,
+                                      const void *residual, void *out, int32_t *sel_idx_out,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* prox_ffn_forward with timing marks: events[0..5] (host array of six
+ * hipEvent_t the caller created) are recorded on the stream before the input
+ * selection, the proxy GEMV, the top-k, the gate/up GEMV and the down
+ * projection, and after the down projection, so that hipEventElapsedTime of
+ * consecutive pairs gives each step's duration on the device.  Without Stage 1
+ * (k == 0 or k == F) events[1] and events[2] coincide. */
+prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w,
+                                   const prox_proxy *p, float input_keep, float ffn_sparsity, void *out,
+                                   int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream, hipEvent_t *events);
+
+/* Stage 1 alone: the mask, and optionally the fp32 channel scores.
+ *   sel_idx_out: device int32 [k] ascending (k from prox_counts);
+ *   scores_out:  nullable device fp32 [F] (score_j as above).
+ * Requires k < F (k == F needs no Stage 1). */
+prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights *w,
+                               const prox_proxy *p, float input_keep, float ffn_sparsity,
+                               int32_t *sel_idx_out, float *scores_out, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Top-k of a score vector, the mask-generation step on its own.
+ *   scores [n] device fp32 (finite); sel_idx_out [k] device int32, receives
+ *   the k indices with the largest |scores| (ties: lower index), ascending.
+ *   1 <= n <= 65536, 0 <= k <= n.  workspace, workspace_bytes: unused (the
+ *   selection runs in one workgroup's LDS and registers). */
+prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_idx_out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 2 alone: exact masked SwiGLU on a given mask.
+ *   sel_idx [k] device int32, distinct channels in [0, F) in ascending order;
+ *   out [B][d] device.  0 <= k <= F. */
+prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *w,
+                              const int32_t *sel_idx, int64_t k, void *out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* RMSNorm with unit gain: out = h / sqrt(mean(h^2) + eps), fp32 math, rounded
+ * to the dtype.  h, out [B][d] device (may alias). */
+prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d_model, prox_dtype dtype, float eps,
+                         void *out, hipStream_t stream);
+
+/* A stack of n_layers Prox FFN layers with pre-norm residual adds, in place:
+ *   for l in 0..n_layers-1:  h <- h + FFN_l(RMSNorm(h))
+ * h [B][d] device (dtype of the layers); layers[l], proxies[l] host arrays of
+ * descriptors with identical shapes and dtype.  The workspace must hold
+ * prox_workspace_size(d, F, B, mode) + 256 + B*d*4 bytes (the normalized
+ * input is staged there). */
+prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layers,
+                               const prox_proxy *proxies, int64_t n_layers, float eps,
+                               float input_keep, float ffn_sparsity, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROX_H */
