@@ -141,7 +141,7 @@ SMALL = [
     (8, 16, "f32", 1, "int8_row", 0.5, 0.5),          # smallest supported shape
     (1000, 1040, "bf16", 1, "int8_row", 0.5, 0.7),    # ragged d and F tails
     (2048, 5504, "bf16", 1, "int8_row", 0.3, 0.9),
-    (1536, 3000, "bf16", 3, "int8_row", 0.5, 0.7),
+    (1536, 3008, "bf16", 3, "int8_row", 0.5, 0.7),
     (1024, 2048, "bf16", 5, "int8_row", 0.5, 0.6),
     (1024, 2048, "bf16", 16, "int8_row", 0.5, 0.7),
     (1024, 4096, "bf16", 1, "int4_g128", 0.4, 0.7),
