@@ -16,7 +16,6 @@ constexpr int kMaxBatch = 16;
 constexpr int kMaxBatchInt4 = 4;
 constexpr int kCounters = 1024;          // [0,512): proxy channel blocks, [512,1024): down slices
 constexpr int kTargetProxyBlocks = 1024;
-constexpr int kTargetDownBlocks = 512;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -90,13 +89,11 @@ ProxyPlan proxy_plan(int64_t d, int64_t F, int64_t B, int mode)
 {
     ProxyPlan p;
     p.qbits = mode == PROX_Q_INT4_G128 ? 4 : 8;
-    if (p.qbits == 8) {
-        p.cpl = 4;
+    p.cpl = p.qbits == 8 ? 4 : 8;  // one 32-bit code word per lane per half
+    if (p.qbits == 8)
         p.nb = B == 1 ? 1 : (B <= 4 ? 4 : 16);
-    } else {
-        p.cpl = 8;
+    else
         p.nb = B == 1 ? 1 : 4;
-    }
     p.n_cblocks = ceil_div(F, 64 * p.cpl);
     const int gran = p.qbits == 4 ? 128 : 32;
     const int s_min = ceil_div(d, kMaxSplitRange);
@@ -117,11 +114,7 @@ DownPlan down_plan(int64_t d, int64_t k, int64_t B, prox_dtype t)
     p.vec = 16 / elem_bytes(t);
     p.cols = 64 * p.vec;
     p.n_slices = ceil_div(d, p.cols);
-    int s = ceil_div(kTargetDownBlocks, p.n_slices);
-    const int s_k = (int)(k / 16);  // at least ~16 rows per split
-    if (k >= 0 && s > s_k) s = s_k;
-    if (s < 1) s = 1;
-    p.S = s;
+    p.S = ceil_div(k > 0 ? k : 1, 16 * kDownWaves);  // 16 ranks per wave
     p.nb = B >= 4 ? 4 : (int)B;
     return p;
 }
@@ -142,7 +135,7 @@ struct Workspace {
 Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
 {
     const ProxyPlan pp = proxy_plan(d, F, B, mode);
-    const int down_s_max = ceil_div(kTargetDownBlocks, ceil_div(d, 64 * 8));
+    const int down_s_max = 2 * ceil_div(F, 16 * kDownWaves);  // 4-token passes use half-size workgroups
     size_t off = 0;
     Workspace w;
     char *b = (char *)base;

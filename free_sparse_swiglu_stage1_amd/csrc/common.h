@@ -61,41 +61,118 @@ __device__ __forceinline__ u32x4 ld_stream(const void *p)
     return __builtin_nontemporal_load((const u32x4 *)p);
 }
 
+// ------------------------------------------------- cross-workgroup data
+// Partial results handed from one workgroup to another within a kernel are
+// stored and loaded as relaxed agent-scope atomics: each access is coherent
+// across the XCDs' L2 caches on its own, so no release/acquire fence (which
+// would write back and invalidate the whole L2) is needed.  The writer waits
+// for its stores to complete before taking its ticket (publish_and_ticket).
+__device__ __forceinline__ void store_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two consecutive floats (8-byte aligned) as one 64-bit coherent access:
+// half the instructions of two 32-bit ones, and the reads cost a fraction.
+__device__ __forceinline__ void store_agent2(float *p, float a, float b)
+{
+    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void load_agent2(const float *p, float &a, float &b)
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    a = __uint_as_float((uint32_t)v);
+    b = __uint_as_float((uint32_t)(v >> 32));
+}
+
+// All threads call after their store_agent()s.  Returns true in exactly one
+// workgroup of the `n` that share `counter`: the last to arrive, which then
+// resets the counter for the next use.
+__device__ __forceinline__ bool publish_and_ticket(uint32_t *counter, uint32_t n, int *s_flag)
+{
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = (t == n - 1);
+        if (t == n - 1) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// wave-uniform value in a scalar register
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // ---------------------------------------------------------------- silu
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------- reductions
-__device__ __forceinline__ float wave_sum(float v)
+// Cross-lane steps use DPP (row shifts within 16-lane rows, then row
+// broadcasts), which run at VALU speed; lane 63 ends with the full result.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, false);
 }
-
-__device__ __forceinline__ uint32_t wave_and(uint32_t v)
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dppf(float old, float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v &= (uint32_t)__shfl_xor((int)v, o, kWave);
-    return v;
+    return __uint_as_float(dpp<CTRL, ROWMASK>(__float_as_uint(old), __float_as_uint(v)));
 }
-
-__device__ __forceinline__ uint32_t wave_or(uint32_t v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, kWave);
-    return v;
-}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
 // inclusive prefix sum within a wave
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = (uint32_t)__shfl_up((int)v, o, kWave);
-        if (lane >= o) v += t;
-    }
+    v += dpp<kRowShr1>(0u, v);
+    v += dpp<kRowShr2>(0u, v);
+    v += dpp<kRowShr4>(0u, v);
+    v += dpp<kRowShr8>(0u, v);
+    v += dpp<kRowBcast15, 0xA>(0u, v);
+    v += dpp<kRowBcast31, 0xC>(0u, v);
     return v;
+}
+
+// wave-wide reductions; the result is uniform (scalar)
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dppf<kRowShr1>(0.0f, v);
+    v += dppf<kRowShr2>(0.0f, v);
+    v += dppf<kRowShr4>(0.0f, v);
+    v += dppf<kRowShr8>(0.0f, v);
+    v += dppf<kRowBcast15, 0xA>(0.0f, v);
+    v += dppf<kRowBcast31, 0xC>(0.0f, v);
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t v)
+{
+    v &= dpp<kRowShr1>(~0u, v);
+    v &= dpp<kRowShr2>(~0u, v);
+    v &= dpp<kRowShr4>(~0u, v);
+    v &= dpp<kRowShr8>(~0u, v);
+    v &= dpp<kRowBcast15, 0xA>(~0u, v);
+    v &= dpp<kRowBcast31, 0xC>(~0u, v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+    v |= dpp<kRowShr1>(0u, v);
+    v |= dpp<kRowShr2>(0u, v);
+    v |= dpp<kRowShr4>(0u, v);
+    v |= dpp<kRowShr8>(0u, v);
+    v |= dpp<kRowBcast15, 0xA>(0u, v);
+    v |= dpp<kRowBcast31, 0xC>(0u, v);
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Exclusive prefix sum over the block in thread order; returns the block
@@ -106,13 +183,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
     constexpr int NW = NT / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    uint32_t incl = wave_incl_scan(v);
+    const uint32_t incl = wave_incl_scan(v);
     if (lane == kWave - 1) scratch[wid] = incl;
     __syncthreads();
     uint32_t base = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        uint32_t s = scratch[w];
+        const uint32_t s = scratch[w];
         base += (w < wid) ? s : 0u;
         tot += s;
     }
@@ -125,11 +202,10 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_and_or(uint32_t a, uint32_t o, uint32_t *scratch, uint32_t *or_out)
 {
     constexpr int NW = NT / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     a = wave_and(a);
     o = wave_or(o);
-    if (lane == 0) {
+    if ((threadIdx.x & (kWave - 1)) == 0) {
         scratch[wid] = a;
         scratch[NW + wid] = o;
     }

@@ -20,6 +20,10 @@ struct ProxyPlan {
     int S;          // number of input splits
 };
 
+// Waves per down-projection workgroup (single token; half for 4-token
+// passes); each wave holds 16 selected rows.
+constexpr int kDownWaves = 16;
+
 // Launch shape of the down projection (K4).
 struct DownPlan {
     int vec;        // columns per lane (16-byte loads)

@@ -3,12 +3,17 @@
 // channel mask.  Keys are magnitudes' IEEE bit patterns, whose unsigned order
 // is the order of the magnitudes.
 //
-// Each thread holds KPT keys for the contiguous index run [tid*KPT, tid*KPT+KPT)
-// in registers.  The k-th largest key T is found by MSB-first radix select
-// in LDS; digit passes start below the bits all keys share (AND/OR reduction),
-// so peaked score distributions do not pile their LDS atomics on a few bins.
-// The caller then selects key > T, plus the first `need_eq` keys == T in index
-// order.
+// Ownership is wave-contiguous: wave w holds the indices
+// [w*64*KPT, (w+1)*64*KPT), lane l's slot r being index w*64*KPT + r*64 + l,
+// so every register load is a coalesced 256-byte wave access and the ordered
+// compaction needs only ballots within a wave plus one scan over waves.
+//
+// The k-th largest key T is found by MSB-first radix select over the bit
+// window where the keys differ (bits all keys share, above and below, are
+// skipped), 9 bits per pass.  The LDS histogram has 16 copies, one per
+// (lane mod 16), so lanes of a wave that land in the same bin are spread over
+// copies: same-address LDS atomics serialize, and score distributions are
+// peaked enough that a single copy would make them the bottleneck.
 #pragma once
 
 #include "common.h"
@@ -20,117 +25,154 @@ struct SelectResult {
     uint32_t need_eq;  // how many keys equal to T are selected (lowest indices)
 };
 
+constexpr int kDigit = 9;
+constexpr int kBins = 1 << kDigit;
+constexpr int kCopies = 16;
+
 struct SelectSmem {
-    uint32_t hist[2048];
+    uint32_t hist[kCopies][kBins];
     uint32_t scratch[64];
     uint32_t found[2];
 };
 
-// n valid keys in total; keys beyond n (idx >= n) are ignored.  1 <= k <= n.
-template <int NT, int KPT, int DIGIT>
+template <int KPT>
+__device__ __forceinline__ int slot_index(int r)
+{
+    return (threadIdx.x >> 6) * 64 * KPT + r * 64 + (threadIdx.x & 63);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive scan of one value per wave (in wave order) and the block total.
+template <int NT>
+__device__ __forceinline__ uint32_t waves_excl_scan(uint32_t wave_val, uint32_t *scratch, uint32_t *total)
+{
+    constexpr int NW = NT / kWave;
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) scratch[wid] = wave_val;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t s = scratch[w];
+        before += (w < wid) ? s : 0u;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return before;
+}
+
+// n valid keys in total; slots with index >= n are ignored.  1 <= k <= n.
+template <int NT, int KPT>
 __device__ SelectResult block_select_kth(const uint32_t (&key)[KPT], int n, int k, SelectSmem &sm)
 {
-    static_assert((1 << DIGIT) % NT == 0 || NT % (1 << DIGIT) == 0, "digit/thread mismatch");
-    constexpr int NBINS = 1 << DIGIT;
+    static_assert(NT >= kBins, "one thread per bin");
     const int tid = threadIdx.x;
-    const int base = tid * KPT;
-
     uint32_t a = 0xFFFFFFFFu, o = 0u;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-        if (base + r < n) {
+        if (slot_index<KPT>(r) < n) {
             a &= key[r];
             o |= key[r];
         }
     uint32_t all_or;
-    uint32_t all_and = block_and_or<NT>(a, o, sm.scratch, &all_or);
-    uint32_t diff = all_and ^ all_or;
+    const uint32_t all_and = block_and_or<NT>(a, o, sm.scratch, &all_or);
+    const uint32_t diff = all_and ^ all_or;
     SelectResult res;
     if (diff == 0u) {  // every key equal
         res.T = all_and;
         res.need_eq = (uint32_t)k;
         return res;
     }
-    int cursor = 31 - __clz(diff);  // highest bit that is not common
-    uint32_t known_mask = (cursor == 31) ? 0u : ~((2u << cursor) - 1u);
-    uint32_t prefix = all_and & known_mask;
+    int cursor = 31 - __clz(diff);       // highest bit where keys differ
+    const int lowest = __ffs(diff) - 1;  // lowest bit where keys differ
+    uint32_t known = (cursor == 31) ? 0u : ~((2u << cursor) - 1u);
+    known |= (1u << lowest) - 1u;        // common bits below the window
+    uint32_t prefix = all_and & known;
     uint32_t remaining = (uint32_t)k;
+    uint32_t *flat = &sm.hist[0][0];
+    const int copy = tid & (kCopies - 1);
 
-    while (cursor >= 0) {
-        const int width = (cursor + 1 < DIGIT) ? cursor + 1 : DIGIT;
+    while (cursor >= lowest) {
+        const int span = cursor - lowest + 1;
+        const int width = span < kDigit ? span : kDigit;
         const int shift = cursor + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
         const int nb = 1 << width;
-        for (int b = tid; b < nb; b += NT) sm.hist[b] = 0u;
+        for (int e = tid; e < kCopies * kBins; e += NT) flat[e] = 0u;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KPT; ++r)
-            if (base + r < n && (key[r] & known_mask) == prefix)
-                atomicAdd(&sm.hist[(key[r] >> shift) & dmask], 1u);
+            if (slot_index<KPT>(r) < n && (key[r] & known) == prefix)
+                atomicAdd(&sm.hist[copy][(key[r] >> shift) & dmask], 1u);
         __syncthreads();
-        // bins in descending digit order: thread t owns bins [nb-1-t*BPT, nb-t*BPT)
-        constexpr int BPT = (NBINS + NT - 1) / NT;
-        uint32_t local = 0;
+        // thread t < nb owns bin nb-1-t (descending digit order)
+        uint32_t h = 0;
+        const int bin = nb - 1 - tid;
+        if (bin >= 0)
 #pragma unroll
-        for (int q = 0; q < BPT; ++q) {
-            int bin = nb - 1 - (tid * BPT + q);
-            if (bin >= 0) local += sm.hist[bin];
-        }
+            for (int c = 0; c < kCopies; ++c) h += sm.hist[c][bin];
         uint32_t tot;
-        uint32_t above = block_excl_scan<NT>(local, sm.scratch, &tot);
-#pragma unroll
-        for (int q = 0; q < BPT; ++q) {
-            int bin = nb - 1 - (tid * BPT + q);
-            if (bin >= 0) {
-                uint32_t h = sm.hist[bin];
-                if (above < remaining && remaining <= above + h) {
-                    sm.found[0] = (uint32_t)bin;
-                    sm.found[1] = above;
-                }
-                above += h;
-            }
+        const uint32_t above = block_excl_scan<NT>(h, sm.scratch, &tot);
+        if (bin >= 0 && above < remaining && remaining <= above + h) {
+            sm.found[0] = (uint32_t)bin;
+            sm.found[1] = above;
         }
         __syncthreads();
         const uint32_t digit = sm.found[0];
         remaining -= sm.found[1];
         prefix |= digit << shift;
-        known_mask |= dmask << shift;
+        known |= dmask << shift;
         cursor = shift - 1;
-        __syncthreads();
     }
     res.T = prefix;
     res.need_eq = remaining;
     return res;
 }
 
-// Selection flags for this thread's KPT keys, in index order, given the
-// threshold.  Returns a bit mask (bit r = key r selected).
+// Selection of this thread's slots given the threshold: returns a bit mask
+// (bit r = slot r selected) and, per selected slot, its rank among the
+// selected indices in ascending index order (pos[r]).
 template <int NT, int KPT>
 __device__ uint64_t block_select_flags(const uint32_t (&key)[KPT], int n, SelectResult sr, SelectSmem &sm,
-                                       uint32_t *n_selected_before, uint32_t *n_selected_total)
+                                       uint32_t (&pos)[KPT])
 {
-    const int base = threadIdx.x * KPT;
-    uint32_t eq = 0;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) eq += (base + r < n && key[r] == sr.T) ? 1u : 0u;
-    uint32_t eq_tot;
-    uint32_t eq_before = block_excl_scan<NT>(eq, sm.scratch, &eq_tot);
-    uint64_t flags = 0;
-    uint32_t cnt = 0;
+    uint64_t eqm[KPT];
+    uint32_t eq_wave = 0;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-        if (base + r >= n) continue;
-        bool s = key[r] > sr.T;
-        if (key[r] == sr.T) {
-            s = eq_before < sr.need_eq;
-            ++eq_before;
-        }
-        if (s) {
-            flags |= 1ull << r;
-            ++cnt;
-        }
+        eqm[r] = __ballot(slot_index<KPT>(r) < n && key[r] == sr.T);
+        eq_wave += (uint32_t)__popcll(eqm[r]);
     }
-    *n_selected_before = block_excl_scan<NT>(cnt, sm.scratch, n_selected_total);
+    uint32_t eq_tot;
+    uint32_t eq_before = waves_excl_scan<NT>(eq_wave, sm.scratch, &eq_tot);
+    uint64_t selm[KPT];
+    uint32_t sel_wave = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const bool valid = slot_index<KPT>(r) < n;
+        bool s = valid && key[r] > sr.T;
+        if (valid && key[r] == sr.T) s = (eq_before + lanes_below(eqm[r])) < sr.need_eq;
+        eq_before += (uint32_t)__popcll(eqm[r]);
+        selm[r] = __ballot(s);
+        sel_wave += (uint32_t)__popcll(selm[r]);
+    }
+    uint32_t sel_tot;
+    uint32_t sel_before = waves_excl_scan<NT>(sel_wave, sm.scratch, &sel_tot);
+    uint64_t flags = 0;
+    const uint64_t me = 1ull << (threadIdx.x & 63);
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        if (selm[r] & me) {
+            flags |= 1ull << r;
+            pos[r] = sel_before + lanes_below(selm[r]);
+        }
+        sel_before += (uint32_t)__popcll(selm[r]);
+    }
     return flags;
 }
 

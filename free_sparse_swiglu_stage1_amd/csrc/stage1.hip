@@ -22,24 +22,30 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
 {
     __shared__ SelectSmem sm;
     const int b = blockIdx.x;
-    const int base = threadIdx.x * KPT;
     if (b == 0)
         for (int c = threadIdx.x; c < n_counters; c += 1024) counters[c] = 0u;
     const T *xb = x + (int64_t)b * d;
     float v[KPT];
     uint32_t key[KPT];
 #pragma unroll
+    for (int r = 0; r < KPT; ++r) {  // all loads issued before any use
+        const int i = slot_index<KPT>(r);
+        v[r] = elem<T>::load(xb, i < d ? i : d - 1);
+    }
+#pragma unroll
     for (int r = 0; r < KPT; ++r) {
-        v[r] = (base + r < d) ? elem<T>::load(xb, base + r) : 0.0f;
+        if (slot_index<KPT>(r) >= d) v[r] = 0.0f;
         key[r] = __float_as_uint(v[r]) & 0x7FFFFFFFu;
     }
-    SelectResult sr = block_select_kth<1024, KPT, 11>(key, d, k_in, sm);
-    uint32_t before, total;
-    uint64_t fl = block_select_flags<1024, KPT>(key, d, sr, sm, &before, &total);
+    SelectResult sr = block_select_kth<1024, KPT>(key, d, k_in, sm);
+    uint32_t pos[KPT];
+    uint64_t fl = block_select_flags<1024, KPT>(key, d, sr, sm, pos);
     float *ob = xh + (int64_t)b * d;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r)
-        if (base + r < d) ob[base + r] = ((fl >> r) & 1ull) ? v[r] : 0.0f;
+    for (int r = 0; r < KPT; ++r) {
+        const int i = slot_index<KPT>(r);
+        if (i < d) ob[i] = ((fl >> r) & 1ull) ? v[r] : 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -48,64 +54,34 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
 // Grid (F/CB channel blocks, S input splits).  A workgroup owns CB channels
 // (gate and up) and the inputs [s*R, s*R+R).  Its prologue compacts the
 // inputs some token kept into an LDS list; the main loop streams only those
-// inputs' code runs (skipped inputs are never read), each wave taking every
-// 4th listed input and each lane CPL consecutive channels.  The four waves'
-// sums are added in LDS in a fixed order and stored as this split's partial
-// g~ / u~; the last split to finish a channel block (atomic ticket) adds the
-// partials in split order, applies the per-channel scale (int8), and writes
+// inputs' code runs (skipped inputs are never read).  Each wave takes every
+// 4th listed input, 16 inputs in flight, and each lane one 32-bit word of
+// codes per half (4 int8 channels or 8 int4 channels).  The four waves' sums
+// are added in LDS in a fixed order into this split's partial g~ / u~; the
+// last split to finish a channel block (atomic ticket) adds the partials in
+// split order, applies the per-channel scale (int8), and writes
 // score_j = sum_b |silu(g~_bj) u~_bj|.  Bitwise deterministic.
 //
 // int4-g128: codes are biased nibbles (q + 8); per 128-input group each lane
-// accumulates sum x*(q+8) and sum x, and at the group end adds
-// scale_g * (acc - 8 * sum x) to its running total.
+// accumulates sum x*(q+8) and sum x, and when the group changes adds
+// scale_g * (acc - 8 * sum x) to its running total; the group scales of the
+// workgroup's channels are staged in LDS by the prologue.
 // ------------------------------------------------------------------------
-template <int QBITS, int CPL>
-struct CodeLoad;
-// int8, 16 channels per lane: 16 bytes
-template <> struct CodeLoad<8, 16> {
-    static __device__ __forceinline__ void get(const uint8_t *p, float *q)
+template <int QBITS>
+struct Codes;
+template <> struct Codes<8> {  // 4 signed bytes -> channels c..c+3
+    static constexpr int CPL = 4;
+    static __device__ __forceinline__ void decode(uint32_t w, float *q)
     {
-        u32x4 v = ld_stream(p);
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) q[a * 4 + n] = (float)(int8_t)(w[a] >> (8 * n));
-    }
-};
-// int8, 4 channels per lane: 4 bytes
-template <> struct CodeLoad<8, 4> {
-    static __device__ __forceinline__ void get(const uint8_t *p, float *q)
-    {
-        uint32_t w = __builtin_nontemporal_load((const uint32_t *)p);
 #pragma unroll
         for (int n = 0; n < 4; ++n) q[n] = (float)(int8_t)(w >> (8 * n));
     }
 };
-// int4 (biased nibbles), 16 channels per lane: 8 bytes.  Byte p holds
-// channel 2p (low nibble) and 2p+1 (high nibble).
-template <> struct CodeLoad<4, 16> {
-    static __device__ __forceinline__ void get(const uint8_t *p, float *q)
+template <> struct Codes<4> {  // 8 biased nibbles; byte p holds channels 2p (low), 2p+1 (high)
+    static constexpr int CPL = 8;
+    static __device__ __forceinline__ void decode(uint32_t w, float *q)
     {
-        u32x2 v = __builtin_nontemporal_load((const u32x2 *)p);
-        uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            uint32_t lo = w[a] & 0x0F0F0F0Fu, hi = (w[a] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                q[a * 8 + 2 * n] = (float)((lo >> (8 * n)) & 0xFFu);
-                q[a * 8 + 2 * n + 1] = (float)((hi >> (8 * n)) & 0xFFu);
-            }
-        }
-    }
-};
-// int4, 8 channels per lane: 4 bytes
-template <> struct CodeLoad<4, 8> {
-    static __device__ __forceinline__ void get(const uint8_t *p, float *q)
-    {
-        uint32_t w = __builtin_nontemporal_load((const uint32_t *)p);
-        uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             q[2 * n] = (float)((lo >> (8 * n)) & 0xFFu);
@@ -114,7 +90,7 @@ template <> struct CodeLoad<4, 8> {
     }
 };
 
-template <int QBITS, int CPL, int NB>
+template <int QBITS, int NB>
 __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh, int B, int d, int F,
                                                     const uint8_t *__restrict__ codes,
                                                     const float *__restrict__ scales, int R, int S,
@@ -122,10 +98,13 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
                                                     uint32_t *__restrict__ counters)
 {
     constexpr int NT = 256;
-    constexpr int CB = 64 * CPL;            // channels per workgroup
+    constexpr int CPL = Codes<QBITS>::CPL;
+    constexpr int CB = 64 * CPL;                 // channels per workgroup
+    constexpr int U = 16;                        // listed inputs in flight per wave
+    constexpr int NG = kMaxSplitRange / 128;     // int4 groups per split
     __shared__ int li[kMaxSplitRange];
     __shared__ float lx[kMaxSplitRange * NB];
-    __shared__ int gstart[kMaxSplitRange / 128 + 1];
+    __shared__ float gsc[QBITS == 4 ? NG : 1][2][QBITS == 4 ? CB : 1];
     __shared__ uint32_t scr[64];
     __shared__ float red[4][2][CB];
     __shared__ int s_last;
@@ -134,22 +113,34 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
     const int cb = blockIdx.x, s = blockIdx.y;
     const int i0 = s * R;
     const int i1 = min(d, i0 + R);
-    const int64_t half_bytes = (int64_t)F * QBITS / 8;  // bytes of one half (gate or up) of a code row
+    const int64_t half_bytes = (int64_t)F * QBITS / 8;  // one half (gate or up) of a code row
+    const int c = cb * CB + lane * CPL;                  // first channel of this lane
+    const bool active = c < F;
+    const int cc = active ? c : 0;
 
-    // ---- prologue: list of inputs some token kept, with their x values
+    // ---- prologue: int4 group scales of this block, and the kept-input list
+    if (QBITS == 4) {
+        const int ng = (i1 - i0 + 127) / 128;
+        for (int e = tid; e < ng * 2 * CB; e += NT) {
+            const int g = e / (2 * CB), h = (e / CB) & 1, jj = e % CB, j = cb * CB + jj;
+            const float v = scales[((int64_t)(i0 / 128 + g) * 2 + h) * F + (j < F ? j : F - 1)];
+            gsc[g][h][jj] = (j < F) ? v : 0.0f;
+        }
+    }
     int nk = 0;
     for (int c0 = i0; c0 < i1; c0 += NT) {
         const int i = c0 + tid;
         float xv[NB];
         bool any = false;
 #pragma unroll
+        for (int b = 0; b < NB; ++b) xv[b] = xh[(int64_t)(b < B ? b : 0) * d + (i < i1 ? i : i1 - 1)];
+#pragma unroll
         for (int b = 0; b < NB; ++b) {
-            xv[b] = (i < i1 && b < B) ? xh[(int64_t)b * d + i] : 0.0f;
+            if (!(i < i1 && b < B)) xv[b] = 0.0f;
             any |= xv[b] != 0.0f;
         }
         uint32_t tot;
-        uint32_t pos = block_excl_scan<NT>(any ? 1u : 0u, scr, &tot);
-        if (QBITS == 4 && i < i1 && ((i - i0) & 127) == 0) gstart[(i - i0) >> 7] = nk + (int)pos;
+        const uint32_t pos = block_excl_scan<NT>(any ? 1u : 0u, scr, &tot);
         if (any) {
             li[nk + pos] = i;
 #pragma unroll
@@ -157,108 +148,77 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
         }
         nk += (int)tot;
     }
-    const int ngroups = (i1 - i0 + 127) / 128;
-    if (QBITS == 4 && tid == 0) gstart[ngroups] = nk;
     __syncthreads();
 
     // ---- main loop
-    const int c = cb * CB + lane * CPL;  // first channel of this lane
-    const bool active = c < F;
-    const int cc = active ? c : 0;
     float acc[NB][2][CPL];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int n = 0; n < CPL; ++n) acc[b][0][n] = acc[b][1][n] = 0.0f;
-
-    const uint8_t *colg = codes + (int64_t)cc * QBITS / 8;
-    if (QBITS == 8) {
-        constexpr int U = (CPL >= 16) ? 4 : 8;  // rows in flight per wave
-        int t = wv;
-        for (; t + 4 * (U - 1) < nk; t += 4 * U) {
-            float qg[U][CPL], qu[U][CPL];
+    float ga[NB][2][CPL], sx[NB];  // int4: current group's sums
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint8_t *row = colg + (int64_t)li[t + 4 * u] * 2 * half_bytes;
-                CodeLoad<QBITS, CPL>::get(row, qg[u]);
-                CodeLoad<QBITS, CPL>::get(row + half_bytes, qu[u]);
+    for (int b = 0; b < NB; ++b) {
+        sx[b] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < CPL; ++n) ga[b][0][n] = ga[b][1][n] = 0.0f;
+    }
+    int cur_g = 0;
+    auto flush_group = [&](int g) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float bias = 8.0f * sx[b];
+#pragma unroll
+            for (int n = 0; n < CPL; ++n) {
+                acc[b][0][n] = fmaf(gsc[g][0][lane * CPL + n], ga[b][0][n] - bias, acc[b][0][n]);
+                acc[b][1][n] = fmaf(gsc[g][1][lane * CPL + n], ga[b][1][n] - bias, acc[b][1][n]);
+                ga[b][0][n] = ga[b][1][n] = 0.0f;
             }
+            sx[b] = 0.0f;
+        }
+    };
+
+    const uint8_t *colp = codes + (int64_t)cc * QBITS / 8;
+    for (int t0 = wv; t0 < nk; t0 += 4 * U) {
+        uint32_t wg[U], wu[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 4 * u;
+            if (t < nk) {
+                const uint8_t *row = colp + (int64_t)li[t] * 2 * half_bytes;
+                wg[u] = __builtin_nontemporal_load((const uint32_t *)row);
+                wu[u] = __builtin_nontemporal_load((const uint32_t *)(row + half_bytes));
+            }
+        }
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const float xv = lx[(t + 4 * u) * NB + b];
-#pragma unroll
-                    for (int n = 0; n < CPL; ++n) {
-                        acc[b][0][n] = fmaf(xv, qg[u][n], acc[b][0][n]);
-                        acc[b][1][n] = fmaf(xv, qu[u][n], acc[b][1][n]);
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 4 * u;
+            if (t < nk) {
+                float qg[CPL], qu[CPL];
+                Codes<QBITS>::decode(wg[u], qg);
+                Codes<QBITS>::decode(wu[u], qu);
+                if (QBITS == 4) {
+                    const int g = (li[t] - i0) >> 7;
+                    if (g != cur_g) {
+                        flush_group(cur_g);
+                        cur_g = g;
                     }
                 }
-        }
-        for (; t < nk; t += 4) {
-            float qg[CPL], qu[CPL];
-            const uint8_t *row = colg + (int64_t)li[t] * 2 * half_bytes;
-            CodeLoad<QBITS, CPL>::get(row, qg);
-            CodeLoad<QBITS, CPL>::get(row + half_bytes, qu);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float xv = lx[t * NB + b];
-#pragma unroll
-                for (int n = 0; n < CPL; ++n) {
-                    acc[b][0][n] = fmaf(xv, qg[n], acc[b][0][n]);
-                    acc[b][1][n] = fmaf(xv, qu[n], acc[b][1][n]);
-                }
-            }
-        }
-    } else {
-        const int g0 = i0 / 128;
-        for (int g = 0; g < ngroups; ++g) {
-            float ga[NB][2][CPL], sx[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                sx[b] = 0.0f;
-#pragma unroll
-                for (int n = 0; n < CPL; ++n) ga[b][0][n] = ga[b][1][n] = 0.0f;
-            }
-            const int te = gstart[g + 1];
-            for (int t = gstart[g] + wv; t < te; t += 4) {
-                float qg[CPL], qu[CPL];
-                const uint8_t *row = colg + (int64_t)li[t] * 2 * half_bytes;
-                CodeLoad<QBITS, CPL>::get(row, qg);
-                CodeLoad<QBITS, CPL>::get(row + half_bytes, qu);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const float xv = lx[t * NB + b];
-                    sx[b] += xv;
+                    if (QBITS == 4) sx[b] += xv;
+                    float(&dst)[2][CPL] = (QBITS == 4) ? ga[b] : acc[b];
 #pragma unroll
                     for (int n = 0; n < CPL; ++n) {
-                        ga[b][0][n] = fmaf(xv, qg[n], ga[b][0][n]);
-                        ga[b][1][n] = fmaf(xv, qu[n], ga[b][1][n]);
-                    }
-                }
-            }
-            if (gstart[g] < te) {
-                const float *scg = scales + ((int64_t)(g0 + g) * 2) * F + cc;
-                float sg[CPL], su[CPL];
-#pragma unroll
-                for (int n = 0; n < CPL; n += 4) {
-                    float4 a = *(const float4 *)(scg + n);
-                    float4 e = *(const float4 *)(scg + F + n);
-                    sg[n] = a.x; sg[n + 1] = a.y; sg[n + 2] = a.z; sg[n + 3] = a.w;
-                    su[n] = e.x; su[n + 1] = e.y; su[n + 2] = e.z; su[n + 3] = e.w;
-                }
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const float bias = 8.0f * sx[b];
-#pragma unroll
-                    for (int n = 0; n < CPL; ++n) {
-                        acc[b][0][n] = fmaf(sg[n], ga[b][0][n] - bias, acc[b][0][n]);
-                        acc[b][1][n] = fmaf(su[n], ga[b][1][n] - bias, acc[b][1][n]);
+                        dst[0][n] = fmaf(xv, qg[n], dst[0][n]);
+                        dst[1][n] = fmaf(xv, qu[n], dst[1][n]);
                     }
                 }
             }
         }
     }
+    if (QBITS == 4) flush_group(cur_g);
 
     // ---- combine the four waves (fixed order), one token at a time
     for (int b = 0; b < B && b < NB; ++b) {
@@ -271,39 +231,51 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
         for (int e = tid; e < 2 * CB; e += NT) {
             const int h = e / CB, jj = e % CB, j = cb * CB + jj;
             if (j < F) {
-                float v = ((red[0][h][jj] + red[1][h][jj]) + red[2][h][jj]) + red[3][h][jj];
-                part[(((int64_t)s * B + b) * 2 + h) * F + j] = v;
+                const float v = ((red[0][h][jj] + red[1][h][jj]) + red[2][h][jj]) + red[3][h][jj];
+                store_agent(&part[(((int64_t)s * B + b) * 2 + h) * F + j], v);
             }
         }
         __syncthreads();
     }
 
-    // ---- last split of this channel block reduces the partials
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[cb], 1u) == (uint32_t)(S - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    // ---- the last split of this channel block reduces the partials
+    if (!publish_and_ticket(&counters[cb], (uint32_t)S, &s_last)) return;
+    constexpr int QC = (NB >= 16) ? 2 : (NB >= 4 ? 8 : 32);  // splits per batch of loads
     for (int jj = tid; jj < CB; jj += NT) {
         const int j = cb * CB + jj;
         if (j >= F) continue;
-        float sc = 0.0f;
-        for (int b = 0; b < B; ++b) {
-            float g = 0.0f, u = 0.0f;
-            for (int q = 0; q < S; ++q) {
-                g += __builtin_nontemporal_load(&part[(((int64_t)q * B + b) * 2 + 0) * F + j]);
-                u += __builtin_nontemporal_load(&part[(((int64_t)q * B + b) * 2 + 1) * F + j]);
-            }
-            if (QBITS == 8) {
-                g *= scales[j];
-                u *= scales[F + j];
-            }
-            sc += fabsf(silu(g) * u);
+        float g[NB], u[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) g[b] = u[b] = 0.0f;
+        for (int q0 = 0; q0 < S; q0 += QC) {
+            float vg[QC][NB], vu[QC][NB];
+#pragma unroll
+            for (int qq = 0; qq < QC; ++qq)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int q = q0 + qq;
+                    const bool ok = q < S && b < B;
+                    const int64_t o = (((int64_t)(ok ? q : 0) * B + (ok ? b : 0)) * 2) * F + j;
+                    vg[qq][b] = load_agent(&part[o]);
+                    vu[qq][b] = load_agent(&part[o + F]);
+                    if (!ok) vg[qq][b] = vu[qq][b] = 0.0f;
+                }
+#pragma unroll
+            for (int qq = 0; qq < QC; ++qq)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    g[b] += vg[qq][b];
+                    u[b] += vu[qq][b];
+                }
         }
+        const float sg = (QBITS == 8) ? scales[j] : 1.0f;
+        const float su = (QBITS == 8) ? scales[F + j] : 1.0f;
+        float sc = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (b < B) sc += fabsf(silu(g[b] * sg) * (u[b] * su));
         score[j] = sc;
     }
-    if (tid == 0) counters[cb] = 0u;
 }
 
 // ------------------------------------------------------------------------
@@ -316,19 +288,20 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ sc
                                                     int32_t *__restrict__ sel)
 {
     __shared__ SelectSmem sm;
-    const int base = threadIdx.x * KPT;
     uint32_t key[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) key[r] = (base + r < n) ? (__float_as_uint(score[base + r]) & 0x7FFFFFFFu) : 0u;
-    SelectResult sr = block_select_kth<1024, KPT, 11>(key, n, k, sm);
-    uint32_t before, total;
-    uint64_t fl = block_select_flags<1024, KPT>(key, n, sr, sm, &before, &total);
+    for (int r = 0; r < KPT; ++r) {  // all loads issued before any use
+        const int i = slot_index<KPT>(r);
+        key[r] = __float_as_uint(score[i < n ? i : n - 1]);
+    }
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) key[r] = (slot_index<KPT>(r) < n) ? (key[r] & 0x7FFFFFFFu) : 0u;
+    SelectResult sr = block_select_kth<1024, KPT>(key, n, k, sm);
+    uint32_t pos[KPT];
+    uint64_t fl = block_select_flags<1024, KPT>(key, n, sr, sm, pos);
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-        if ((fl >> r) & 1ull) {
-            if (before < (uint32_t)k) sel[before] = base + r;
-            ++before;
-        }
+        if (((fl >> r) & 1ull) && pos[r] < (uint32_t)k) sel[pos[r]] = slot_index<KPT>(r);
 }
 
 // ------------------------------------------------------------------------
@@ -358,17 +331,15 @@ hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int 
                         const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st)
 {
     dim3 grid(pl.n_cblocks, pl.S);
-#define PX(Q, C, N) proxy_kernel<Q, C, N><<<grid, 256, 0, st>>>(xh, B, d, F, codes, scales, pl.R, pl.S, part, score, counters)
+#define PX(Q, N) proxy_kernel<Q, N><<<grid, 256, 0, st>>>(xh, B, d, F, codes, scales, pl.R, pl.S, part, score, counters)
     if (pl.qbits == 8) {
-        if (pl.cpl == 4 && pl.nb == 1) PX(8, 4, 1);
-        else if (pl.cpl == 16 && pl.nb == 1) PX(8, 16, 1);
-        else if (pl.cpl == 4 && pl.nb == 4) PX(8, 4, 4);
-        else if (pl.cpl == 4 && pl.nb == 16) PX(8, 4, 16);
+        if (pl.nb == 1) PX(8, 1);
+        else if (pl.nb == 4) PX(8, 4);
+        else if (pl.nb == 16) PX(8, 16);
         else return hipErrorInvalidValue;
     } else {
-        if (pl.cpl == 8 && pl.nb == 1) PX(4, 8, 1);
-        else if (pl.cpl == 16 && pl.nb == 1) PX(4, 16, 1);
-        else if (pl.cpl == 8 && pl.nb == 4) PX(4, 8, 4);
+        if (pl.nb == 1) PX(4, 1);
+        else if (pl.nb == 4) PX(4, 4);
         else return hipErrorInvalidValue;
     }
 #undef PX
@@ -380,7 +351,7 @@ hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream
     const int kpt = (n + 1023) / 1024;
 #define TK(K) \
     if (kpt <= K) { topk_kernel<K><<<1, 1024, 0, st>>>(score, n, k, sel); return hipGetLastError(); }
-    TK(4) TK(8) TK(16) TK(32) TK(64)
+    TK(1) TK(2) TK(4) TK(8) TK(16) TK(32) TK(64)
 #undef TK
     return hipErrorInvalidValue;
 }

@@ -15,129 +15,211 @@ namespace prox {
 // them with x (staged once per workgroup in LDS as fp32) and writes
 // s[b][r] = silu(g) * u in fp32.
 // ------------------------------------------------------------------------
+// x of a workgroup in registers: up to kStageRegs 16-byte vectors per thread.
+constexpr int kStageRegs = 2;
+
+template <typename T, int NB>
+__device__ __forceinline__ void load_rows_regs(const T *__restrict__ x, int B, int d, u32x4 (&xr)[kStageRegs])
+{
+    constexpr int V = vec16<T>::N;
+    const int nvec = NB * d / V;
+#pragma unroll
+    for (int q = 0; q < kStageRegs; ++q) {
+        int e = threadIdx.x + q * 256;
+        e = min(e, nvec - 1);
+        const int b = (e * V) / d;
+        xr[q] = *(const u32x4 *)(x + (int64_t)(b < B ? b : 0) * d + (e * V - b * d));
+    }
+}
+
+template <typename T, int NB>
+__device__ __forceinline__ void store_rows_lds(const u32x4 (&xr)[kStageRegs], int B, int d, float *xs)
+{
+    constexpr int V = vec16<T>::N;
+    const int nvec = NB * d / V;
+#pragma unroll
+    for (int q = 0; q < kStageRegs; ++q) {
+        const int e = threadIdx.x + q * 256;
+        if (e < nvec) {
+            float f[V];
+            vec16<T>::unpack(xr[q], f);
+            const bool live = (e * V) / d < B;
+#pragma unroll
+            for (int i = 0; i < V; ++i) xs[e * V + i] = live ? f[i] : 0.0f;
+        }
+    }
+    __syncthreads();
+}
+
+// Stage rows [0, min(B, NB)) of a [B][d] tensor into LDS as fp32 (rows up to
+// NB zero-filled), 16-byte loads, all of a thread's loads issued before use.
+template <typename T, int NB>
+__device__ __forceinline__ void stage_rows_f32(const T *__restrict__ x, int B, int d, float *xs)
+{
+    constexpr int V = vec16<T>::N;
+    constexpr int PER = 2;  // 16-byte loads per thread per batch
+    const int nvec = NB * d / V;
+    for (int e0 = threadIdx.x; e0 < nvec; e0 += 256 * PER) {
+        u32x4 v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            int e = e0 + q * 256;
+            e = e < nvec ? e : nvec - 1;
+            const int b = (e * V) / d;
+            v[q] = *(const u32x4 *)(x + (int64_t)(b < B ? b : 0) * d + (e * V - b * d));
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = e0 + q * 256;
+            if (e < nvec) {
+                float f[V];
+                vec16<T>::unpack(v[q], f);
+                const bool live = (e * V) / d < B;
+#pragma unroll
+                for (int i = 0; i < V; ++i) xs[e * V + i] = live ? f[i] : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 template <typename T, int NB>
 __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d,
                                                      const T *__restrict__ w_gu, const int32_t *__restrict__ sel,
                                                      int k, float *__restrict__ s_sp, int32_t *__restrict__ iota_out)
 {
     constexpr int V = vec16<T>::N;  // elements per 16-byte load
-    constexpr int UNR = 8;          // 16-byte chunks in flight per row
+    constexpr int UNR = 8;          // 16-byte vectors per lane per pass (two rows: 2*UNR loads)
     extern __shared__ float xs[];   // [NB][d]
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    for (int e = tid; e < NB * d; e += 256) {
-        const int b = e / d;
-        xs[e] = (b < B) ? elem<T>::load(x, (int64_t)b * d + (e - b * d)) : 0.0f;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int r = blockIdx.x * 4 + wv;  // one selected channel per wave
+    const bool live = r < k;
+    const int j = live ? (sel ? sel[r] : r) : (sel ? sel[0] : 0);
+    if (iota_out && live && lane == 0) iota_out[r] = r;
+    const T *grow = w_gu + (int64_t)j * 2 * d;
+    const T *urow = grow + d;
+    const int nv = d / V;  // 16-byte vectors per row
+
+    // x first (vmcnt retires in order: waiting for x must not wait for the rows)
+    const bool x_in_regs = NB * nv <= 256 * kStageRegs;
+    u32x4 xr[kStageRegs];
+    if (x_in_regs) load_rows_regs<T, NB>(x, B, d, xr);
+    // first pass of both rows, every load issued (clamped index), no branches
+    u32x4 vg[UNR], vu[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+        const int vi = min(lane + u * 64, nv - 1);
+        vg[u] = ld_stream(grow + vi * V);
+        vu[u] = ld_stream(urow + vi * V);
     }
-    __syncthreads();
-    const int nwaves = gridDim.x * 4;
-    for (int r = blockIdx.x * 4 + wv; r < k; r += nwaves) {
-        const int j = sel ? sel[r] : r;
-        if (iota_out && lane == 0) iota_out[r] = r;
-        const T *grow = w_gu + (int64_t)j * 2 * d;
-        const T *urow = grow + d;
-        float ag[NB], au[NB];
+    if (x_in_regs)
+        store_rows_lds<T, NB>(xr, B, d, xs);
+    else
+        stage_rows_f32<T, NB>(x, B, d, xs);
+
+    float ag[NB], au[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) ag[b] = au[b] = 0.0f;
-        for (int e0 = lane * V; e0 < d; e0 += 64 * V * UNR) {
-            u32x4 vg[UNR], vu[UNR];
+    for (int b = 0; b < NB; ++b) ag[b] = au[b] = 0.0f;
+    for (int base = 0; base < nv; base += 64 * UNR) {
+        if (base > 0) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int e = e0 + u * 64 * V;
-                if (e < d) {
-                    vg[u] = ld_stream(grow + e);
-                    vu[u] = ld_stream(urow + e);
-                }
+                const int vi = min(base + lane + u * 64, nv - 1);
+                vg[u] = ld_stream(grow + vi * V);
+                vu[u] = ld_stream(urow + vi * V);
             }
+        }
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int e = e0 + u * 64 * V;
-                if (e < d) {
-                    float fg[V], fu[V];
-                    vec16<T>::unpack(vg[u], fg);
-                    vec16<T>::unpack(vu[u], fu);
+        for (int u = 0; u < UNR; ++u) {
+            const int vi = base + lane + u * 64;
+            if (vi < nv) {
+                float fg[V], fu[V];
+                vec16<T>::unpack(vg[u], fg);
+                vec16<T>::unpack(vu[u], fu);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const float *xb = xs + b * d + e;
+                for (int b = 0; b < NB; ++b) {
+                    const float *xb = xs + b * d + vi * V;
 #pragma unroll
-                        for (int q = 0; q < V; ++q) {
-                            ag[b] = fmaf(fg[q], xb[q], ag[b]);
-                            au[b] = fmaf(fu[q], xb[q], au[b]);
-                        }
+                    for (int q = 0; q < V; ++q) {
+                        ag[b] = fmaf(fg[q], xb[q], ag[b]);
+                        au[b] = fmaf(fu[q], xb[q], au[b]);
                     }
                 }
             }
         }
+    }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const float g = wave_sum(ag[b]);
-            const float u = wave_sum(au[b]);
-            if (lane == 0 && b < B) s_sp[(int64_t)b * k + r] = silu(g) * u;
-        }
+    for (int b = 0; b < NB; ++b) {
+        const float g = wave_sum(ag[b]);
+        const float u = wave_sum(au[b]);
+        if (live && lane == 0 && b < B) s_sp[(int64_t)b * k + r] = silu(g) * u;
     }
 }
 
 // ------------------------------------------------------------------------
 // K4: down projection over the selected rows of W_down^T [F][d].
-// Grid (column slices of 64*VEC outputs, S rank splits).  Each wave takes
-// every 4th selected channel of its split and adds s[b][r] * W_down^T[j][cols]
-// into VEC columns per lane; the four waves are combined in LDS in a fixed
-// order into this split's partial; the last split of a slice (atomic ticket)
-// adds the partials in split order, adds the residual if any, and stores.
+// Grid (column slices of 64*VEC outputs, S rank splits); a workgroup of
+// NW waves owns the ranks [s*16*NW, (s+1)*16*NW) of its slice, each wave 16
+// consecutive ranks, all 16 rows in flight at once: one vector load brings
+// the wave's 16 channel indices and s values, then the 16 row segments are
+// loaded (16-byte loads, VEC columns per lane) and accumulated.  The waves
+// are combined in LDS in a fixed order into this split's partial; the last
+// split of a slice (atomic ticket) adds the partials -- the splits in NW
+// groups in parallel, each in split order, then the groups in order -- adds
+// the residual if any, rounds and stores.
 // ------------------------------------------------------------------------
-template <typename T, int NB>
-__global__ __launch_bounds__(256) void down_kernel(const float *__restrict__ s_sp, int B, int k,
-                                                   const T *__restrict__ wdt, const int32_t *__restrict__ sel,
-                                                   int d, int S, float *__restrict__ part,
-                                                   const T *residual, T *out, uint32_t *__restrict__ counters)
+constexpr int kDownRowsPerWave = 16;
+
+template <typename T, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__ s_sp, int B, int k,
+                                                       const T *__restrict__ wdt, const int32_t *__restrict__ sel,
+                                                       int d, int S, float *__restrict__ part,
+                                                       const T *residual, T *out, uint32_t *__restrict__ counters)
 {
+    constexpr int NT = 64 * NW;
     constexpr int V = vec16<T>::N;
     constexpr int COLS = 64 * V;
-    constexpr int UNR = 8;
-    __shared__ float red[4][NB][COLS];
+    constexpr int U = kDownRowsPerWave;
+    __shared__ float red[NW][NB][COLS];
     __shared__ int s_last;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int sl = blockIdx.x, s = blockIdx.y;
     const int c = sl * COLS + lane * V;
     const bool active = c < d;
-    const int r0 = (int)(((int64_t)k * s) / S), r1 = (int)(((int64_t)k * (s + 1)) / S);
+    const int cc = active ? c : 0;
+    const int rw0 = (s * NW + wv) * U;                    // this wave's first rank
+    const int nr = max(0, min(U, k - rw0));               // ranks it holds (wave-uniform)
+    // lanes 0..15 fetch the channel index and s values of rank rw0 + lane
+    const int rl = rw0 + (lane & (U - 1));
+    const int rlc = rl < k ? rl : k - 1;
+    const int jl = sel ? sel[rlc] : rlc;
+    float sl_v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sl_v[b] = s_sp[(int64_t)(b < B ? b : 0) * k + rlc];
     float acc[NB][V];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[b][q] = 0.0f;
-
-    int r = r0 + wv;
-    for (; r + 4 * (UNR - 1) < r1; r += 4 * UNR) {
-        u32x4 w[UNR];
+    if (nr > 0) {
+        u32x4 w[U];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int rr = r + 4 * u;
-            const int j = sel ? sel[rr] : rr;
-            w[u] = active ? ld_stream(wdt + (int64_t)j * d + c) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < U; ++u) {
+            const int j = __builtin_amdgcn_readlane(jl, u);
+            if (u < nr) w[u] = ld_stream(wdt + (int64_t)j * d + cc);
         }
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            float f[V];
-            vec16<T>::unpack(w[u], f);
+        for (int u = 0; u < U; ++u) {
+            if (u < nr) {
+                float f[V];
+                vec16<T>::unpack(w[u], f);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float sv = (b < B) ? s_sp[(int64_t)b * k + r + 4 * u] : 0.0f;
+                for (int b = 0; b < NB; ++b) {
+                    const float sv = (b < B) ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sl_v[b]), u)) : 0.0f;
 #pragma unroll
-                for (int q = 0; q < V; ++q) acc[b][q] = fmaf(sv, f[q], acc[b][q]);
+                    for (int q = 0; q < V; ++q) acc[b][q] = fmaf(sv, f[q], acc[b][q]);
+                }
             }
-        }
-    }
-    for (; r < r1; r += 4) {
-        const int j = sel ? sel[r] : r;
-        u32x4 w = u32x4{0u, 0u, 0u, 0u};
-        if (active) w = ld_stream(wdt + (int64_t)j * d + c);
-        float f[V];
-        vec16<T>::unpack(w, f);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const float sv = (b < B) ? s_sp[(int64_t)b * k + r] : 0.0f;
-#pragma unroll
-            for (int q = 0; q < V; ++q) acc[b][q] = fmaf(sv, f[q], acc[b][q]);
         }
     }
 
@@ -146,28 +228,60 @@ __global__ __launch_bounds__(256) void down_kernel(const float *__restrict__ s_s
 #pragma unroll
         for (int q = 0; q < V; ++q) red[wv][b][lane * V + q] = acc[b][q];
     __syncthreads();
-    for (int e = tid; e < NB * COLS; e += 256) {
-        const int b = e / COLS, cc = e % COLS, col = sl * COLS + cc;
+    for (int e = tid; e < NB * COLS / 2; e += NT) {  // column pairs
+        const int b = e / (COLS / 2), ci = 2 * (e % (COLS / 2)), col = sl * COLS + ci;
         if (b < B && col < d) {
-            const float v = ((red[0][b][cc] + red[1][b][cc]) + red[2][b][cc]) + red[3][b][cc];
-            part[((int64_t)s * B + b) * d + col] = v;
+            float v0 = red[0][b][ci], v1 = red[0][b][ci + 1];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                v0 += red[w][b][ci];
+                v1 += red[w][b][ci + 1];
+            }
+            store_agent2(&part[((int64_t)s * B + b) * d + col], v0, v1);
         }
     }
-    __threadfence();
+    if (!publish_and_ticket(&counters[sl], (uint32_t)S, &s_last)) return;
+    // thread t: column pair t % (COLS/2), split group t / (COLS/2)
+    constexpr int PAIRS = COLS / 2;
+    constexpr int GROUPS = NT / PAIRS;
+    constexpr int QB = 16;  // splits loaded per batch
+    const int pair = tid % PAIRS, grp = tid / PAIRS;
+    const int col0 = sl * COLS + pair * 2;
+    const int qa = (S * grp) / GROUPS, qe = (S * (grp + 1)) / GROUPS;
+    float (*gsum)[NB][COLS] = reinterpret_cast<float (*)[NB][COLS]>(&red[0][0][0]);  // [GROUPS][NB][COLS]
+    static_assert(GROUPS <= NW, "group sums must fit the reduction buffer");
     __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[sl], 1u) == (uint32_t)(S - 1));
+    for (int b = 0; b < NB; ++b) {
+        float y0 = 0.0f, y1 = 0.0f;
+        if (b < B && col0 < d && qa < qe) {
+            for (int q0 = qa; q0 < qe; q0 += QB) {
+                float v0[QB], v1[QB];
+#pragma unroll
+                for (int i = 0; i < QB; ++i) {
+                    const int q = min(q0 + i, qe - 1);
+                    load_agent2(&part[((int64_t)q * B + b) * d + col0], v0[i], v1[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < QB; ++i)
+                    if (q0 + i < qe) {
+                        y0 += v0[i];
+                        y1 += v1[i];
+                    }
+            }
+        }
+        gsum[grp][b][pair * 2] = y0;
+        gsum[grp][b][pair * 2 + 1] = y1;
+    }
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int e = tid; e < B * COLS; e += 256) {
-        const int b = e / COLS, col = sl * COLS + e % COLS;
-        if (col >= d) continue;
-        float y = 0.0f;
-        for (int q = 0; q < S; ++q) y += __builtin_nontemporal_load(&part[((int64_t)q * B + b) * d + col]);
+    for (int e = tid; e < B * COLS; e += NT) {
+        const int b = e / COLS, ci = e % COLS, col = sl * COLS + ci;
+        if (col >= d || b >= NB) continue;
+        float y = gsum[0][b][ci];
+#pragma unroll
+        for (int g = 1; g < GROUPS; ++g) y += gsum[g][b][ci];
         if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
         elem<T>::store(out, (int64_t)b * d + col, y);
     }
-    if (tid == 0) counters[sl] = 0u;
 }
 
 // out = residual (or 0): the k == 0 case
@@ -213,8 +327,7 @@ static hipError_t gateup_t(const void *x, int B, int d, const void *w_gu, const 
                            int32_t *iota_out, hipStream_t st)
 {
     if (k <= 0) return hipSuccess;
-    int blocks = (k + 7) / 8;  // two channels per wave
-    if (blocks < 1) blocks = 1;
+    const int blocks = (k + 3) / 4;  // one channel per wave
     // x of up to 4 tokens staged in LDS as fp32, within 64 KB
     const int tb = (4 * d * (int)sizeof(float) <= 65536) ? 4 : 1;
     for (int b0 = 0; b0 < B; b0 += tb) {
@@ -244,6 +357,7 @@ static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, co
                          int d, float *part, const void *residual, void *out, uint32_t *counters, hipStream_t st)
 {
     dim3 grid(pl.n_slices, pl.S);
+    dim3 grid4(pl.n_slices, 2 * pl.S);  // half-size workgroups for 4-token passes
     // tokens in passes of at most 4 (a pass re-reads the selected rows)
     for (int b0 = 0; b0 < B; b0 += 4) {
         const int nb = (B - b0 >= 4) ? 4 : B - b0;
@@ -251,9 +365,11 @@ static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, co
         const T *res = residual ? (const T *)residual + (int64_t)b0 * d : nullptr;
         T *o = (T *)out + (int64_t)b0 * d;
         if (nb == 1)
-            down_kernel<T, 1><<<grid, 256, 0, st>>>(sp, 1, k, (const T *)wdt, sel, d, pl.S, part, res, o, counters);
+            down_kernel<T, 1, kDownWaves><<<grid, 64 * kDownWaves, 0, st>>>(sp, 1, k, (const T *)wdt, sel, d, pl.S,
+                                                                         part, res, o, counters);
         else
-            down_kernel<T, 4><<<grid, 256, 0, st>>>(sp, nb, k, (const T *)wdt, sel, d, pl.S, part, res, o, counters);
+            down_kernel<T, 4, kDownWaves / 2><<<grid4, 32 * kDownWaves, 0, st>>>(sp, nb, k, (const T *)wdt, sel, d,
+                                                                              2 * pl.S, part, res, o, counters);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
