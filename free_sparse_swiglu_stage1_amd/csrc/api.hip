@@ -26,7 +26,7 @@ int elem_bytes(prox_dtype t) { return t == PROX_F32 ? 4 : 2; }
 
 prox_status check_shape(int64_t d, int64_t F)
 {
-    if (d < 8 || d > 16384 || F < 16 || F > 65536) return PROX_ERR_UNSUPPORTED;
+    if (d < 8 || d > 16384 || F < 16 || F > 65520) return PROX_ERR_UNSUPPORTED;
     if (d % 8 != 0 || F % 16 != 0) return PROX_ERR_UNSUPPORTED;
     return PROX_OK;
 }
@@ -364,7 +364,7 @@ prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_id
 {
     (void)workspace;
     (void)workspace_bytes;
-    if (n < 1 || n > 65536 || k < 0 || k > n) return PROX_ERR_INVALID_ARG;
+    if (n < 1 || n > 65535 || k < 0 || k > n) return PROX_ERR_INVALID_ARG;
     if (bad_ptr(scores) || bad_ptr(sel_idx_out)) return PROX_ERR_INVALID_ARG;
     if (k == 0) return PROX_OK;
     return hip_status(launch_topk(scores, (int)n, (int)k, sel_idx_out, stream));

@@ -23,7 +23,7 @@
  *    C++ exception crosses this interface.
  *  - Device pointers must be 16-byte aligned.  x and out must not alias.
  *  - Shapes: d_model % 8 == 0 (int4-g128 proxy: % 128), d_ff % 16 == 0,
- *    8 <= d_model <= 16384, 16 <= d_ff <= 65536, 1 <= batch <= 16
+ *    8 <= d_model <= 16384, 16 <= d_ff <= 65520, 1 <= batch <= 16
  *    (int4-g128 proxy: batch <= 4); other sizes return PROX_ERR_UNSUPPORTED.
  *  - One workspace must not be used by two calls that may run concurrently.
  *    Its contents need no initialization and mean nothing between calls.
@@ -179,7 +179,7 @@ prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights 
 /* Top-k of a score vector, the mask-generation step on its own.
  *   scores [n] device fp32 (finite); sel_idx_out [k] device int32, receives
  *   the k indices with the largest |scores| (ties: lower index), ascending.
- *   1 <= n <= 65536, 0 <= k <= n.  workspace, workspace_bytes: unused (the
+ *   1 <= n <= 65535, 0 <= k <= n.  workspace, workspace_bytes: unused (the
  *   selection runs in one workgroup's LDS and registers). */
 prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_idx_out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -67,6 +67,7 @@ def test_counts_reject_bad_fractions(keep, sp):
     (4096, 14336, "int8_row", 0), (8192, 28672, "int4_g128", 0), (4100, 14336, "int8_row", B.ERR_UNSUPPORTED),
     (4096, 14330, "int8_row", B.ERR_UNSUPPORTED), (4104, 14336, "int4_g128", B.ERR_UNSUPPORTED),
     (32768, 14336, "int8_row", B.ERR_UNSUPPORTED), (4096, 131072, "int8_row", B.ERR_UNSUPPORTED),
+    (4096, 65536, "int8_row", B.ERR_UNSUPPORTED), (4096, 65520, "int8_row", 0),
 ])
 def test_proxy_sizes(d, F, mode, status):
     if status == 0:
@@ -149,6 +150,7 @@ def test_other_entry_points_reject(lib):
     assert lib.prox_topk(v(FAKE), 0, 0, v(FAKE), None, 0, None) == B.ERR_INVALID_ARG
     assert lib.prox_topk(v(FAKE), 100, 101, v(FAKE), None, 0, None) == B.ERR_INVALID_ARG
     assert lib.prox_topk(v(FAKE), 70000, 5, v(FAKE), None, 0, None) == B.ERR_INVALID_ARG
+    assert lib.prox_topk(v(FAKE), 65536, 5, v(FAKE), None, 0, None) == B.ERR_INVALID_ARG
     assert lib.prox_stage1_select(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.0, v(FAKE + 64), None,
                                   v(FAKE + 256), 1 << 40, None) == B.ERR_INVALID_ARG  # k == F: no Stage 1
     assert lib.prox_rmsnorm(v(FAKE), 1, 4096, 9, 1e-5, v(FAKE), None) == B.ERR_UNSUPPORTED
