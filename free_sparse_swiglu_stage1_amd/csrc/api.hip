@@ -14,7 +14,11 @@ namespace {
 
 constexpr int kMaxBatch = 16;
 constexpr int kMaxBatchInt4 = 4;
-constexpr int kCounters = 1024;          // [0,512): proxy channel blocks, [512,1024): down slices
+// The workspace starts with ticket counters that must be zero between
+// calls: [0,511) proxy channel blocks, 511 the single-token Stage 1's score
+// ticket, [512,1024) down slices.  Each is reset by its last arriver.
+constexpr int kCounters = 1024;
+constexpr int kZeroWords = kCounters;
 constexpr int kTargetProxyBlocks = 1024;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -135,14 +139,19 @@ struct Workspace {
 Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
 {
     const ProxyPlan pp = proxy_plan(d, F, B, mode);
+    size_t part_rows = (size_t)pp.S * B;
+    if (fused_supported(B, d, F)) {
+        const FusedPlan fp = fused_plan(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
+        if ((size_t)fp.S > part_rows) part_rows = fp.S;
+    }
     const int down_s_max = 2 * ceil_div(F, 16 * kDownWaves);  // 4-token passes use half-size workgroups
     size_t off = 0;
     Workspace w;
     char *b = (char *)base;
     auto take = [&](size_t n) { char *p = b ? b + off : nullptr; off += align256(n); return p; };
-    w.counters = (uint32_t *)take(sizeof(uint32_t) * kCounters);
+    w.counters = (uint32_t *)take(sizeof(uint32_t) * kZeroWords);
     w.xh = (float *)take(sizeof(float) * B * d);
-    w.proxy_part = (float *)take(sizeof(float) * (size_t)pp.S * B * 2 * F);
+    w.proxy_part = (float *)take(sizeof(float) * part_rows * 2 * F);
     w.score = (float *)take(sizeof(float) * F);
     w.sel = (int32_t *)take(sizeof(int32_t) * F);
     w.s_sp = (float *)take(sizeof(float) * B * F);
@@ -168,9 +177,18 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
                        hipEvent_t *ev = nullptr)
 {
     const int64_t d = w->d_model, F = w->d_ff;
+    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    if (fused_supported(B, d, F)) {  // one kernel; its counters are zero on entry
+        TRY_HIP(mark(ev, 0, st));
+        TRY_HIP(launch_stage1_fused(dt, p->mode == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
+                                    (const uint8_t *)p->codes, (const float *)p->scales, ws.proxy_part, score, sel,
+                                    ws.counters, st));
+        TRY_HIP(mark(ev, 1, st));
+        return hip_status(mark(ev, 2, st));
+    }
     const ProxyPlan pp = proxy_plan(d, F, B, p->mode);
     TRY_HIP(mark(ev, 0, st));
-    TRY_HIP(launch_xselect(w->dtype == PROX_F32 ? 0 : 1, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
+    TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
                            kCounters, st));
     TRY_HIP(mark(ev, 1, st));
     TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes, (const float *)p->scales,
@@ -193,10 +211,10 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
-    TRY_HIP(launch_gateup(dt, x, (int)B, (int)d, w->w_gu, sel, (int)k, ws.s_sp, iota_out, st));
+    TRY_HIP(launch_gateup(dt, x, (int)B, (int)d, (int)w->d_ff, w->w_gu, sel, (int)k, ws.s_sp, iota_out, st));
     TRY_HIP(mark(ev, 4, st));
     const DownPlan dp = down_plan(d, k, B, w->dtype);
-    TRY_HIP(launch_down(dt, dp, ws.s_sp, (int)B, (int)k, w->w_down_t, sel, (int)d, ws.down_part, residual, out,
+    TRY_HIP(launch_down(dt, dp, ws.s_sp, (int)B, (int)k, w->w_down_t, sel, (int)d, (int)w->d_ff, ws.down_part, residual, out,
                         ws.counters + 512, st));
     return hip_status(mark(ev, 5, st));
 }
@@ -307,6 +325,13 @@ prox_status prox_workspace_size(int64_t d, int64_t F, int64_t B, prox_qmode mode
     if (s != PROX_OK) return s;
     *bytes = layout(d, F, B, mode, nullptr).bytes;
     return PROX_OK;
+}
+
+prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (bad_ptr(workspace)) return PROX_ERR_INVALID_ARG;
+    if (workspace_bytes < sizeof(uint32_t) * kZeroWords) return PROX_ERR_WORKSPACE;
+    return hip_status(launch_zero_u32((uint32_t *)workspace, kZeroWords, stream));
 }
 
 prox_status prox_ffn_forward(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,

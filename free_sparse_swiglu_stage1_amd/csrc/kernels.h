@@ -33,16 +33,35 @@ struct DownPlan {
     int nb;         // tokens per pass
 };
 
+// Single-token Stage 1 in one kernel (stage1_fused.hip).
+constexpr int kFusedMaxD = 8192;       // inputs (d_model)
+constexpr int kFusedMaxF = 16384;      // channels (d_ff): all scores fit in LDS
+constexpr int kFusedScoreSlot = 511;   // counter of finished channel blocks
+
+struct FusedPlan {
+    int n_cblocks;  // ceil(F / channels per workgroup)
+    int R;          // inputs per split
+    int S;          // number of input splits
+};
+
+FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
+bool fused_supported(int64_t B, int64_t d, int64_t F);
+hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
+                               const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
+                               uint32_t *counters, hipStream_t st);
+
 hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
                           int n_counters, hipStream_t st);
 hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
                         const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st);
 hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st);
 
-hipError_t launch_gateup(int dtype, const void *x, int B, int d, const void *w_gu, const int32_t *sel, int k,
-                         float *s_sp, int32_t *iota_out, hipStream_t st);
+// Stage 2 clamps every mask entry into [0, F): a malformed mask gives wrong
+// values, never an access outside the weights.
+hipError_t launch_gateup(int dtype, const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel,
+                         int k, float *s_sp, int32_t *iota_out, hipStream_t st);
 hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
-                       const int32_t *sel, int d, float *part, const void *residual, void *out,
+                       const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);

@@ -3,42 +3,43 @@
 // channel mask.  Keys are magnitudes' IEEE bit patterns (sign bit clear),
 // whose unsigned order is the order of the magnitudes.
 //
-// Ownership is wave-contiguous: wave w holds the indices
-// [w*64*KPT, (w+1)*64*KPT), lane l's slot r being index w*64*KPT + r*64 + l,
-// so every register load is a coalesced 256-byte wave access and the ordered
-// compaction needs only ballots within a wave plus one scan over waves.
-//
-// The k-th largest key T is found by MSB-first radix select over the bit
-// window where the keys differ (bits all keys share are skipped).  The first
-// pass takes the top 15 bits of the window at once, into 32768 bins of packed
-// 16-bit counters (64 KB of LDS): with that many bins, keys of nearby value
-// rarely hit the same counter, so the LDS atomics do not serialize, and for
-// bf16-derived keys this one pass decides T.  The at most 16 bits left are
-// resolved over the few remaining candidates with 8-bit passes whose
-// histogram has 16 copies, one per (lane mod 16), to spread equal bins.
+// A workgroup retires about one wave64 instruction per clock, so the cost of
+// a selection is the number of instructions spent per key plus the fixed
+// cost of each pass (LDS clears, barriers).  The design keeps both small:
+//  - keys stay in registers, wave-contiguous: wave w holds the indices
+//    [w*64*KPT, (w+1)*64*KPT), lane l's slot r being index
+//    w*64*KPT + r*64 + l, so a row r of a wave is 64 consecutive indices;
+//  - the k-th largest key T is found by MSB-first radix passes of at most
+//    11 bits (2048 counters, 8 KB of LDS) over the bit window where the
+//    keys differ, stopping as soon as the keys of the crossing bin are
+//    exactly the ones still needed;
+//  - the selection ({key > T} and the lowest-index keys equal to T) is
+//    written as a bitmap, one ballot per row, and compacted in index order
+//    from the bitmap (one scan over words instead of one per key).
 #pragma once
 
 #include "common.h"
 
 namespace prox {
 
+constexpr int kPassBits = 11;
+constexpr int kPassBins = 1 << kPassBits;
+
 struct SelectResult {
-    uint32_t T;         // k-th largest key
-    uint32_t need_eq;   // how many keys equal to T are selected (lowest indices)
-    uint32_t count_eq;  // how many keys equal T
+    uint32_t T;         // threshold key
+    uint32_t need_eq;   // keys equal to T to select (lowest indices)
+    uint32_t count_eq;  // keys equal to T; need_eq == count_eq: select key >= T
 };
 
-constexpr int kWideBits = 15;
-constexpr int kNarrowBits = 8;
-constexpr int kCopies = 16;
-
-struct SelectSmem {
-    union {
-        uint32_t wide[1 << (kWideBits - 1)];          // 2^15 16-bit counters, two per word
-        uint32_t narrow[kCopies][1 << kNarrowBits];   // 16 copies of 256 bins
-    };
+// MAXN: the largest key count (a multiple of 64).
+template <int MAXN>
+struct alignas(16) SelectSmem {
+    static constexpr int W = MAXN / 32;  // bitmap words
+    static_assert(MAXN % 64 == 0 && W <= kPassBins, "bitmap sizes");
+    uint32_t hist[kPassBins];  // radix counters; afterwards the bitmap of keys equal to T
+    uint32_t bits[W];          // selection bitmap: bit i of word i/32 = index i selected
     uint32_t scratch[64];
-    uint32_t found[3];
+    uint32_t found[4];
 };
 
 template <int KPT>
@@ -46,6 +47,10 @@ __device__ __forceinline__ int slot_index(int r)
 {
     return (threadIdx.x >> 6) * 64 * KPT + r * 64 + (threadIdx.x & 63);
 }
+
+// A value every lane holds alike, moved to a scalar register so that the
+// branches on it are scalar.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
 {
@@ -72,116 +77,100 @@ __device__ __forceinline__ uint32_t waves_excl_scan(uint32_t wave_val, uint32_t 
     return before;
 }
 
-// The wide pass: 2^15 bins of the 15 bits at `shift`, packed 16-bit
-// counters.  Thread t owns the 2^15/NT bins just below 2^15 - t*2^15/NT (the
-// highest bins go to thread 0), reads its counter words once with 16-byte
-// LDS loads and finds the crossing bin in registers.
-template <int NT, int KPT>
-__device__ __forceinline__ uint32_t wide_pass(const uint32_t (&key)[KPT], int n, int shift, uint32_t &prefix,
-                                              uint32_t &known, uint32_t &remaining, SelectSmem &sm)
+// Bin counts owned in thread order (thread t: bins [t*BPT, (t+1)*BPT)).
+// Finds the bin holding the remaining-th largest key, counting from the top
+// bin down: found[0] = bin, found[1] = keys in higher bins, found[2] = keys
+// in the bin.  Requires 1 <= remaining <= total.  Two barriers.
+template <int NT, int BPT>
+__device__ __forceinline__ void find_crossing(const uint32_t (&h)[BPT], uint32_t remaining, uint32_t *scratch,
+                                              uint32_t *found)
 {
-    constexpr int NWORDS = 1 << (kWideBits - 1);
-    constexpr int WPT = NWORDS / NT;  // counter words per thread
-    static_assert(WPT % 4 == 0, "16-byte LDS accesses");
-    const int tid = threadIdx.x;
-    const int w0 = NWORDS - (tid + 1) * WPT;  // this thread's first word
-    u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.wide[w0]);
-#pragma unroll
-    for (int i = 0; i < WPT / 4; ++i) mine[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    const uint32_t dmask = (1u << kWideBits) - 1u;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        if (slot_index<KPT>(r) < n && (key[r] & known) == prefix) {
-            const uint32_t dg = (key[r] >> shift) & dmask;
-            atomicAdd(&sm.wide[dg >> 1], 1u << ((dg & 1u) * 16u));
-        }
-    }
-    __syncthreads();
-    uint32_t w[WPT];
-#pragma unroll
-    for (int i = 0; i < WPT / 4; ++i) {
-        const u32x4 v = mine[i];
-        w[4 * i] = v.x;
-        w[4 * i + 1] = v.y;
-        w[4 * i + 2] = v.z;
-        w[4 * i + 3] = v.w;
-    }
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) local += (w[i] & 0xFFFFu) + (w[i] >> 16);
-    uint32_t tot;
-    uint32_t above = block_excl_scan<NT>(local, sm.scratch, &tot);
-    if (above < remaining && remaining <= above + local) {
+    for (int i = 0; i < BPT; ++i) local += h[i];
+    const uint32_t incl = wave_incl_scan(local);
+    const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+    if (lane == 0) scratch[wv] = wtot;
+    __syncthreads();
+    uint32_t a = wtot - incl;  // keys in this wave's higher threads
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a += (w > wv) ? scratch[w] : 0u;
+    if (a < remaining && remaining <= a + local) {
         bool done = false;
 #pragma unroll
-        for (int i = WPT - 1; i >= 0; --i) {
-#pragma unroll
-            for (int half = 1; half >= 0; --half) {
-                const uint32_t h = (w[i] >> (16 * half)) & 0xFFFFu;
-                if (!done && above < remaining && remaining <= above + h) {
-                    sm.found[0] = (uint32_t)(2 * (w0 + i) + half);
-                    sm.found[1] = above;
-                    sm.found[2] = h;
-                    done = true;
-                }
-                above += h;
+        for (int i = BPT - 1; i >= 0; --i) {
+            if (!done && a < remaining && remaining <= a + h[i]) {
+                found[0] = (uint32_t)(tid * BPT + i);
+                found[1] = a;
+                found[2] = h[i];
+                done = true;
             }
+            a += h[i];
         }
     }
     __syncthreads();
-    const uint32_t digit = sm.found[0];
-    remaining -= sm.found[1];
-    const uint32_t in_bin = sm.found[2];
-    prefix |= digit << shift;
-    known |= dmask << shift;
-    __syncthreads();
-    return in_bin;
 }
 
-// A narrow pass: bins of `width` (<= 8) bits at `shift` among the keys whose
-// `known` bits equal `prefix`, 16 counter copies.
-template <int NT, int KPT>
-__device__ __forceinline__ uint32_t narrow_pass(const uint32_t (&key)[KPT], int n, int width, int shift,
-                                                uint32_t &prefix, uint32_t &known, uint32_t &remaining,
-                                                SelectSmem &sm)
+// One radix pass: counts the `width` (<= 11) bits at `shift` of the keys
+// whose `known` bits equal `prefix`, finds the crossing bin and narrows the
+// state to it.  Returns the number of keys in that bin.
+template <int NT, int KPT, int MAXN>
+__device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n, int width, int shift,
+                                               uint32_t &prefix, uint32_t &known, uint32_t &remaining,
+                                               SelectSmem<MAXN> &sm)
 {
-    static_assert(NT >= (1 << kNarrowBits), "one thread per bin");
+    constexpr int BPT = kPassBins / NT;
+    static_assert(BPT == 1 || BPT == 2 || BPT == 4, "bins per thread");
     const int tid = threadIdx.x;
-    const uint32_t dmask = (1u << width) - 1u;
-    const int nb = 1 << width;
-    for (int e = tid; e < kCopies * (1 << kNarrowBits); e += NT) (&sm.narrow[0][0])[e] = 0u;
+    uint32_t *mine = &sm.hist[tid * BPT];
+    if (BPT == 4) *reinterpret_cast<u32x4 *>(mine) = u32x4{0u, 0u, 0u, 0u};
+    else if (BPT == 2) *reinterpret_cast<u32x2 *>(mine) = u32x2{0u, 0u};
+    else mine[0] = 0u;
     __syncthreads();
+    const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
     for (int r = 0; r < KPT; ++r)
-        if (slot_index<KPT>(r) < n && (key[r] & known) == prefix)
-            atomicAdd(&sm.narrow[tid & (kCopies - 1)][(key[r] >> shift) & dmask], 1u);
+        if (slot_index<KPT>(r) < n && (key[r] & known) == prefix) atomicAdd(&sm.hist[(key[r] >> shift) & dmask], 1u);
     __syncthreads();
-    const int bin = nb - 1 - tid;  // thread t owns bin nb-1-t
-    uint32_t h = 0;
-    if (bin >= 0)
+    uint32_t h[BPT];
 #pragma unroll
-        for (int q = 0; q < kCopies; ++q) h += sm.narrow[q][bin];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan<NT>(h, sm.scratch, &tot);
-    if (bin >= 0 && above < remaining && remaining <= above + h) {
-        sm.found[0] = (uint32_t)bin;
-        sm.found[1] = above;
-        sm.found[2] = h;
-    }
-    __syncthreads();
-    const uint32_t digit = sm.found[0];
-    remaining -= sm.found[1];
-    const uint32_t in_bin = sm.found[2];
-    prefix |= digit << shift;
+    for (int i = 0; i < BPT; ++i) h[i] = mine[i];
+    find_crossing<NT, BPT>(h, remaining, sm.scratch, sm.found);
+    remaining -= uniform_u32(sm.found[1]);
+    prefix |= uniform_u32(sm.found[0]) << shift;
     known |= dmask << shift;
-    __syncthreads();
-    return in_bin;
+    return uniform_u32(sm.found[2]);
 }
 
-// n valid keys in total; slots with index >= n are ignored.  1 <= k <= n.
-template <int NT, int KPT>
-__device__ SelectResult block_select_kth(const uint32_t (&key)[KPT], int n, int k, SelectSmem &sm)
+// Radix passes over the bits [lowest, cursor] below a known prefix, until
+// the crossing bin holds exactly the keys still needed or every bit is known.
+template <int NT, int KPT, int MAXN>
+__device__ SelectResult radix_select_from(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t known,
+                                          uint32_t remaining, int cursor, int lowest, SelectSmem<MAXN> &sm)
+{
+    uint32_t in_bin = 0;
+    while (cursor >= lowest) {
+        const int span = cursor - lowest + 1;
+        const int width = span < kPassBits ? span : kPassBits;
+        const int shift = cursor + 1 - width;
+        in_bin = radix_pass<NT, KPT, MAXN>(key, n, width, shift, prefix, known, remaining, sm);
+        cursor = shift - 1;
+        if (remaining == in_bin) break;  // the whole bin is selected
+    }
+    // the bin's keys are >= prefix (unknown bits zero), lower keys < prefix,
+    // higher keys > prefix; when every bit is known they all equal prefix
+    SelectResult s;
+    s.T = prefix;
+    s.need_eq = remaining;
+    s.count_eq = in_bin;
+    return s;
+}
+
+// The k-th largest of n keys (1 <= k <= n; slots with index >= n ignored).
+template <int NT, int KPT, int MAXN>
+__device__ SelectResult block_select(const uint32_t (&key)[KPT], int n, int k, SelectSmem<MAXN> &sm)
 {
     uint32_t a = 0xFFFFFFFFu, o = 0u;
 #pragma unroll
@@ -191,98 +180,113 @@ __device__ SelectResult block_select_kth(const uint32_t (&key)[KPT], int n, int 
             o |= key[r];
         }
     uint32_t all_or;
-    const uint32_t all_and = block_and_or<NT>(a, o, sm.scratch, &all_or);
-    const uint32_t diff = all_and ^ all_or;
-    SelectResult res;
-    if (diff == 0u) {  // every key equal
-        res.T = all_and;
-        res.need_eq = (uint32_t)k;
-        res.count_eq = (uint32_t)n;
-        return res;
+    const uint32_t all_and = uniform_u32(block_and_or<NT>(a, o, sm.scratch, &all_or));
+    const uint32_t diff = all_and ^ uniform_u32(all_or);
+    if (diff == 0u) {  // every key equal: the k lowest indices
+        SelectResult s;
+        s.T = all_and;
+        s.need_eq = (uint32_t)k;
+        s.count_eq = (uint32_t)n;
+        return s;
     }
-    int cursor = 31 - __clz(diff);       // highest bit where keys differ
-    const int lowest = __ffs(diff) - 1;  // lowest bit where keys differ
+    const int cursor = 31 - __clz(diff);  // highest bit where keys differ
+    const int lowest = __ffs(diff) - 1;   // lowest bit where keys differ
     uint32_t known = (cursor == 31) ? 0u : ~((2u << cursor) - 1u);
-    known |= (1u << lowest) - 1u;        // common bits below the window
-    uint32_t prefix = all_and & known;
-    uint32_t remaining = (uint32_t)k;
-    // wide pass: the 15 bits from the top of the window (extending below the
-    // window when it is narrower; those bits are common to every key)
-    int shift = max(cursor + 1 - kWideBits, 0);
-    uint32_t in_bin;
-    if (cursor + 1 >= kWideBits) {
-        known &= ~(((1u << kWideBits) - 1u) << shift);
-        prefix &= known;
-        in_bin = wide_pass<NT, KPT>(key, n, shift, prefix, known, remaining, sm);
-        cursor = shift - 1;
-    } else {
-        in_bin = (uint32_t)n;
-    }
-    while (cursor >= lowest) {
-        const int span = cursor - lowest + 1;
-        const int width = span < kNarrowBits ? span : kNarrowBits;
-        shift = cursor + 1 - width;
-        in_bin = narrow_pass<NT, KPT>(key, n, width, shift, prefix, known, remaining, sm);
-        cursor = shift - 1;
-    }
-    res.T = prefix;
-    res.need_eq = remaining;
-    res.count_eq = in_bin;  // the last pass's bin holds exactly the keys equal to T
-    return res;
+    known |= (1u << lowest) - 1u;  // common bits below the window
+    return radix_select_from<NT, KPT, MAXN>(key, n, all_and & known, known, (uint32_t)k, cursor, lowest, sm);
 }
 
-// Selection of this thread's slots given the threshold: returns a bit mask
-// (bit r = slot r selected) and, per selected slot, its rank among the
-// selected indices in ascending index order (pos[r]).  When every key equal
-// to T is selected (the usual case), no ranking among equal keys is needed.
-template <int NT, int KPT>
-__device__ uint64_t block_select_flags(const uint32_t (&key)[KPT], int n, SelectResult sr, SelectSmem &sm,
-                                       uint32_t (&pos)[KPT])
+// Keeps the lowest `keep` set bits of m.
+__device__ __forceinline__ uint32_t lowest_set_bits(uint32_t m, uint32_t keep)
 {
-    uint64_t selm[KPT];
-    if (sr.need_eq == sr.count_eq) {
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) selm[r] = __ballot(slot_index<KPT>(r) < n && key[r] >= sr.T);
-    } else {
-        uint64_t eqm[KPT];
-        uint32_t eqc[KPT];
-        uint32_t eq_wave = 0;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) eqm[r] = __ballot(slot_index<KPT>(r) < n && key[r] == sr.T);
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            eqc[r] = eq_wave;
-            eq_wave += (uint32_t)__popcll(eqm[r]);
-        }
-        uint32_t eq_tot;
-        const uint32_t eq_before = waves_excl_scan<NT>(eq_wave, sm.scratch, &eq_tot);
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const bool valid = slot_index<KPT>(r) < n;
-            bool s = valid && key[r] > sr.T;
-            if (valid && key[r] == sr.T) s = (eq_before + eqc[r] + lanes_below(eqm[r])) < sr.need_eq;
-            selm[r] = __ballot(s);
-        }
-    }
-    uint32_t selc[KPT];
-    uint32_t sel_wave = 0;
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        selc[r] = sel_wave;
-        sel_wave += (uint32_t)__popcll(selm[r]);
-    }
-    uint32_t sel_tot;
-    const uint32_t sel_before = waves_excl_scan<NT>(sel_wave, sm.scratch, &sel_tot);
-    uint64_t flags = 0;
-    const uint64_t me = 1ull << (threadIdx.x & 63);
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        if (selm[r] & me) {
-            flags |= 1ull << r;
-            pos[r] = sel_before + selc[r] + lanes_below(selm[r]);
-        }
-    }
-    return flags;
+    if (keep == 0u) return 0u;
+    while ((uint32_t)__popc(m) > keep) m &= ~(0x80000000u >> __clz(m));
+    return m;
 }
+
+// Writes the selection {key > T} and the need_eq lowest-index keys equal to
+// T into sm.bits (words [0, ceil(NT*KPT/32)), every one written).  Lane r
+// keeps row r's ballot and one store per lane writes them all.  Ends with a
+// barrier.
+template <int NT, int KPT, int MAXN>
+__device__ void selection_bitmap(const uint32_t (&key)[KPT], int n, SelectResult s, SelectSmem<MAXN> &sm)
+{
+    static_assert(NT * KPT <= MAXN && KPT <= 64, "rows beyond the bitmap");
+    constexpr int W = SelectSmem<MAXN>::W;
+    const int lane = threadIdx.x & 63;
+    const int row0 = (threadIdx.x >> 6) * 64 * KPT;  // this wave's first index
+    const uint32_t T = uniform_u32(s.T), need_eq = uniform_u32(s.need_eq);
+    const bool all = need_eq == uniform_u32(s.count_eq);
+    // all: key >= T; else key > T here and the equal keys below
+    const uint64_t T1 = all ? (uint64_t)T : (uint64_t)T + 1u;
+    uint64_t mine = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const uint64_t gt = __ballot((slot_index<KPT>(r) < n) & ((uint64_t)key[r] >= T1));
+        mine = (lane == r) ? gt : mine;
+    }
+    if (lane < KPT) *reinterpret_cast<uint64_t *>(&sm.bits[(row0 >> 5) + 2 * lane]) = mine;
+    if (!all) {
+        mine = 0;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const uint64_t eq = __ballot((slot_index<KPT>(r) < n) & (key[r] == T));
+            mine = (lane == r) ? eq : mine;
+        }
+        if (lane < KPT) *reinterpret_cast<uint64_t *>(&sm.hist[(row0 >> 5) + 2 * lane]) = mine;
+    }
+    __syncthreads();
+    if (!all) {  // of the keys equal to T, the need_eq first in index order
+        constexpr int WPT = (W + NT - 1) / NT;
+        const int nw = (n + 31) >> 5;  // words the rows wrote
+        const int w0 = threadIdx.x * WPT;
+        uint32_t m[WPT], cnt = 0;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            m[j] = (w0 + j < nw) ? sm.hist[w0 + j] : 0u;
+            cnt += (uint32_t)__popc(m[j]);
+        }
+        uint32_t tot;
+        uint32_t before = block_excl_scan<NT>(cnt, sm.scratch, &tot);
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const uint32_t keep = before < need_eq ? need_eq - before : 0u;
+            if (m[j] && keep) sm.bits[w0 + j] |= lowest_set_bits(m[j], keep);
+            before += (uint32_t)__popc(m[j]);
+        }
+        __syncthreads();
+    }
+}
+
+// Calls emit(i, pos) for every index i < n set in sm.bits, pos being its
+// rank in ascending index order.
+template <int NT, int MAXN, typename Emit>
+__device__ void emit_bitmap(int n, SelectSmem<MAXN> &sm, Emit emit)
+{
+    constexpr int W = SelectSmem<MAXN>::W;
+    constexpr int WPT = (W + NT - 1) / NT;
+    const int nw = (n + 31) >> 5;
+    const int w0 = threadIdx.x * WPT;
+    uint32_t m[WPT], cnt = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int wj = w0 + j;
+        m[j] = (wj < nw) ? sm.bits[wj] : 0u;
+        if (wj == nw - 1 && (n & 31)) m[j] &= (1u << (n & 31)) - 1u;
+        cnt += (uint32_t)__popc(m[j]);
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan<NT>(cnt, sm.scratch, &tot);
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        uint32_t b = m[j];
+        while (b) {
+            emit(32 * (w0 + j) + (__ffs(b) - 1), pos++);
+            b &= b - 1u;
+        }
+    }
+}
+
+__device__ __forceinline__ bool bitmap_test(const uint32_t *bits, int i) { return (bits[i >> 5] >> (i & 31)) & 1u; }
 
 }  // namespace prox

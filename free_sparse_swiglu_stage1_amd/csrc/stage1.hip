@@ -20,7 +20,7 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
                                                        float *__restrict__ xh, uint32_t *__restrict__ counters,
                                                        int n_counters)
 {
-    __shared__ SelectSmem sm;
+    __shared__ SelectSmem<16384> sm;
     const int b = blockIdx.x;
     if (b == 0)
         for (int c = threadIdx.x; c < n_counters; c += 1024) counters[c] = 0u;
@@ -37,14 +37,13 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
         if (slot_index<KPT>(r) >= d) v[r] = 0.0f;
         key[r] = __float_as_uint(v[r]) & 0x7FFFFFFFu;
     }
-    SelectResult sr = block_select_kth<1024, KPT>(key, d, k_in, sm);
-    uint32_t pos[KPT];
-    uint64_t fl = block_select_flags<1024, KPT>(key, d, sr, sm, pos);
+    const SelectResult sr = block_select<1024, KPT>(key, d, k_in, sm);
+    selection_bitmap<1024, KPT>(key, d, sr, sm);
     float *ob = xh + (int64_t)b * d;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
         const int i = slot_index<KPT>(r);
-        if (i < d) ob[i] = ((fl >> r) & 1ull) ? v[r] : 0.0f;
+        if (i < d) ob[i] = bitmap_test(sm.bits, i) ? v[r] : 0.0f;
     }
 }
 
@@ -287,7 +286,7 @@ template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ score, int n, int k,
                                                     int32_t *__restrict__ sel)
 {
-    __shared__ SelectSmem sm;
+    __shared__ SelectSmem<65536> sm;
     uint32_t key[KPT];
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {  // all loads issued before any use
@@ -296,12 +295,11 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ sc
     }
 #pragma unroll
     for (int r = 0; r < KPT; ++r) key[r] = (slot_index<KPT>(r) < n) ? (key[r] & 0x7FFFFFFFu) : 0u;
-    SelectResult sr = block_select_kth<1024, KPT>(key, n, k, sm);
-    uint32_t pos[KPT];
-    uint64_t fl = block_select_flags<1024, KPT>(key, n, sr, sm, pos);
-#pragma unroll
-    for (int r = 0; r < KPT; ++r)
-        if (((fl >> r) & 1ull) && pos[r] < (uint32_t)k) sel[pos[r]] = slot_index<KPT>(r);
+    const SelectResult sr = block_select<1024, KPT>(key, n, k, sm);
+    selection_bitmap<1024, KPT>(key, n, sr, sm);
+    emit_bitmap<1024>(n, sm, [&](int i, uint32_t pos) {
+        if (pos < (uint32_t)k) sel[pos] = i;
+    });
 }
 
 // ------------------------------------------------------------------------

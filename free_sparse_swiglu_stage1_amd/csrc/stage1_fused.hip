@@ -1,0 +1,332 @@
+// Stage 1 of Prox for one token in a single kernel: input sparsification,
+// proxy gate/up GEMV, channel salience and the top-k channel mask
+// ("Lightweight Proxy Construction").  Fusing the four steps removes three
+// dependent launches, each worth a few microseconds on this device, from a
+// step that streams ~60 MB of codes in ~10 us.
+//
+// Grid (channel blocks, input splits) sized to one wave of workgroups, two
+// per CU; 512 threads.  Every workgroup
+//  1. selects the kept inputs itself (every workgroup takes the same exact
+//     decision on the same keys) and lists those of its input split in LDS,
+//     in ascending order;
+//  2. streams the code rows of those inputs for its CB channels, 32 rows in
+//     flight per wave, one 32-bit code word per lane per half (gate, up);
+//  3. adds its eight waves' sums in LDS in a fixed order and publishes the
+//     split's partial g~ / u~ with coherent 64-bit stores.
+// The last split of a channel block to finish (ticket) adds the partials in
+// split order and publishes score_j = |silu(g~_j) u~_j| for its channels;
+// the last channel block to finish (ticket) loads all F scores and writes
+// the k selected channel indices in ascending order.  Bitwise deterministic.
+//
+// Counters: counters[cb] and counters[kFusedScoreSlot] must be zero on
+// entry; the last arriver of each ticket resets it, so a completed launch
+// leaves them zero again.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "select.h"
+
+namespace prox {
+
+constexpr int kFT = 512;          // threads per workgroup
+constexpr int kFW = kFT / 64;     // waves per workgroup
+constexpr int kFRows = 32;        // kept inputs in flight per wave
+constexpr int kFusedSlots = 512;  // workgroups resident at once (two per CU)
+
+template <int QBITS>
+struct Fused;
+template <> struct Fused<8> {  // 4 signed bytes -> channels c..c+3
+    static constexpr int CPL = 4, RMAX = 1024, GRAN = 32, NG = 1;
+    static __device__ __forceinline__ void decode(uint32_t w, float *q)
+    {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) q[n] = (float)(int8_t)(w >> (8 * n));
+    }
+};
+template <> struct Fused<4> {  // 8 biased nibbles; byte p holds channels 2p (low), 2p+1 (high)
+    static constexpr int CPL = 8, RMAX = 512, GRAN = 128, NG = 512 / 128;
+    static __device__ __forceinline__ void decode(uint32_t w, float *q)
+    {
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            q[2 * n] = (float)((lo >> (8 * n)) & 0xFFu);
+            q[2 * n + 1] = (float)((hi >> (8 * n)) & 0xFFu);
+        }
+    }
+};
+
+template <int QBITS>
+struct FusedSmem {
+    static constexpr int CB = 64 * Fused<QBITS>::CPL;
+    int li[Fused<QBITS>::RMAX];    // this split's kept inputs, ascending
+    float lx[Fused<QBITS>::RMAX];  // their values
+    union {
+        SelectSmem<kFusedMaxF> sel;
+        struct {
+            float red[kFW][2][CB];
+            float gsc[Fused<QBITS>::NG][2][QBITS == 4 ? CB : 1];
+        } p;
+    };
+    int flag;
+};
+
+template <typename T, int QBITS, int KX, int KF>
+__global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restrict__ x, int d, int F, int k_in, int k,
+                                                           const uint8_t *__restrict__ codes,
+                                                           const float *__restrict__ scales, int R, int S,
+                                                           int n_cblocks, float *__restrict__ part,
+                                                           float *__restrict__ score, int32_t *__restrict__ sel,
+                                                           uint32_t *__restrict__ counters)
+{
+    using Q = Fused<QBITS>;
+    constexpr int CPL = Q::CPL;
+    constexpr int CB = 64 * CPL;  // channels per workgroup
+    constexpr int U = kFRows;
+    __shared__ FusedSmem<QBITS> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int cb = blockIdx.x, s = blockIdx.y;
+    const int i0 = s * R, i1 = min(d, i0 + R);
+    const int64_t half_bytes = (int64_t)F * QBITS / 8;
+    const int c = cb * CB + lane * CPL;
+    const int cc = c < F ? c : 0;
+
+    // ---- 1. input selection; x (and the int4 group scales) loaded first
+    constexpr int XR = Q::RMAX / kFT;  // list rows of this split
+    float xv[KX], xr[XR];
+#pragma unroll
+    for (int r = 0; r < KX; ++r) xv[r] = elem<T>::load(x, min(slot_index<KX>(r), d - 1));
+#pragma unroll
+    for (int q = 0; q < XR; ++q) xr[q] = elem<T>::load(x, min(i0 + q * kFT + tid, d - 1));
+    constexpr int GS = QBITS == 4 ? Q::NG * 2 * CB / kFT : 1;  // group scales per thread
+    float gs_reg[GS];
+    if (QBITS == 4) {
+        const int ng = (i1 - i0 + 127) / 128;
+#pragma unroll
+        for (int q = 0; q < GS; ++q) {
+            const int e = tid + q * kFT;
+            const int g = e / (2 * CB), h = (e / CB) & 1, j = min(cb * CB + e % CB, F - 1);
+            gs_reg[q] = scales[((int64_t)(i0 / 128 + min(g, ng - 1)) * 2 + h) * F + j];
+        }
+    }
+    uint32_t key[KX];
+#pragma unroll
+    for (int r = 0; r < KX; ++r) {
+        if (slot_index<KX>(r) >= d) xv[r] = 0.0f;
+        key[r] = __float_as_uint(xv[r]) & 0x7FFFFFFFu;
+    }
+    const SelectResult sr = block_select<kFT, KX>(key, d, k_in, sm.sel);
+    selection_bitmap<kFT, KX>(key, d, sr, sm.sel);
+    int nk = 0;  // the split's kept inputs, listed in ascending order
+#pragma unroll
+    for (int q = 0; q < XR; ++q) {
+        if (q * kFT >= R) break;  // uniform
+        const int i = i0 + q * kFT + tid;
+        const bool kept = i < i1 && bitmap_test(sm.sel.bits, i);
+        const uint64_t m = __ballot(kept);
+        uint32_t tot;
+        const uint32_t before = uniform_u32(waves_excl_scan<kFT>((uint32_t)__popcll(m), sm.sel.scratch, &tot));
+        if (kept) {
+            sm.li[nk + before + lanes_below(m)] = i;
+            sm.lx[nk + before + lanes_below(m)] = xr[q];
+        }
+        nk += (int)uniform_u32(tot);
+    }
+    if (QBITS == 4) {
+#pragma unroll
+        for (int q = 0; q < GS; ++q) {
+            const int e = tid + q * kFT;
+            sm.p.gsc[e / (2 * CB)][(e / CB) & 1][e % CB] = gs_reg[q];
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. proxy GEMV over this split's kept inputs
+    float acc[2][CPL], ga[2][CPL], sx = 0.0f;  // int4: ga, sx = current group's sums
+#pragma unroll
+    for (int n = 0; n < CPL; ++n) acc[0][n] = acc[1][n] = ga[0][n] = ga[1][n] = 0.0f;
+    int cur_g = 0;
+    const uint32_t col_off = (uint32_t)cc * QBITS / 8;  // codes are < 4 GiB: 32-bit offsets
+    const uint32_t row_bytes = 2u * (uint32_t)half_bytes;
+    for (int t0 = wv; t0 < nk; t0 += kFW * U) {
+        uint32_t wg[U], wu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // every load issued (clamped), no branches
+            const int t = min(t0 + kFW * u, nk - 1);
+            const uint32_t o = (uint32_t)sm.li[t] * row_bytes + col_off;
+            wg[u] = __builtin_nontemporal_load((const uint32_t *)(codes + o));
+            wu[u] = __builtin_nontemporal_load((const uint32_t *)(codes + o + (uint32_t)half_bytes));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + kFW * u;
+            if (t < nk) {
+                float qg[CPL], qu[CPL];
+                Q::decode(wg[u], qg);
+                Q::decode(wu[u], qu);
+                const float xk = sm.lx[t];
+                if (QBITS == 4) {
+                    const int g = (sm.li[t] - i0) >> 7;
+                    if (g != cur_g) {  // group change: fold the finished group in
+                        const float bias = 8.0f * sx;
+#pragma unroll
+                        for (int n = 0; n < CPL; ++n) {
+                            acc[0][n] = fmaf(sm.p.gsc[cur_g][0][lane * CPL + n], ga[0][n] - bias, acc[0][n]);
+                            acc[1][n] = fmaf(sm.p.gsc[cur_g][1][lane * CPL + n], ga[1][n] - bias, acc[1][n]);
+                            ga[0][n] = ga[1][n] = 0.0f;
+                        }
+                        sx = 0.0f;
+                        cur_g = g;
+                    }
+                    sx += xk;
+                }
+                float(&dst)[2][CPL] = (QBITS == 4) ? ga : acc;
+#pragma unroll
+                for (int n = 0; n < CPL; ++n) {
+                    dst[0][n] = fmaf(xk, qg[n], dst[0][n]);
+                    dst[1][n] = fmaf(xk, qu[n], dst[1][n]);
+                }
+            }
+        }
+    }
+    if (QBITS == 4) {
+        const float bias = 8.0f * sx;
+#pragma unroll
+        for (int n = 0; n < CPL; ++n) {
+            acc[0][n] = fmaf(sm.p.gsc[cur_g][0][lane * CPL + n], ga[0][n] - bias, acc[0][n]);
+            acc[1][n] = fmaf(sm.p.gsc[cur_g][1][lane * CPL + n], ga[1][n] - bias, acc[1][n]);
+        }
+    }
+
+    // ---- 3. the split's partial: waves added in a fixed order, 64-bit stores
+#pragma unroll
+    for (int n = 0; n < CPL; ++n) {
+        sm.p.red[wv][0][lane * CPL + n] = acc[0][n];
+        sm.p.red[wv][1][lane * CPL + n] = acc[1][n];
+    }
+    __syncthreads();
+    for (int e = tid; e < CB; e += kFT) {  // e = (half, channel pair)
+        const int h = e / (CB / 2), jj = 2 * (e % (CB / 2)), j = cb * CB + jj;
+        if (j < F) {
+            float v0 = sm.p.red[0][h][jj], v1 = sm.p.red[0][h][jj + 1];
+#pragma unroll
+            for (int w = 1; w < kFW; ++w) {
+                v0 += sm.p.red[w][h][jj];
+                v1 += sm.p.red[w][h][jj + 1];
+            }
+            store_agent2(&part[((int64_t)s * 2 + h) * F + j], v0, v1);
+        }
+    }
+    if (!publish_and_ticket(&counters[cb], (uint32_t)S, &sm.flag)) return;
+
+    // ---- the last split of this channel block: scores of its channels
+    for (int e = tid; e < CB; e += kFT) {
+        const int h = e / (CB / 2), jj = 2 * (e % (CB / 2)), j = cb * CB + jj;
+        float v0 = 0.0f, v1 = 0.0f;
+        if (j < F) {
+            for (int q0 = 0; q0 < S; q0 += 16) {
+                float a0[16], a1[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    load_agent2(&part[((int64_t)min(q0 + i, S - 1) * 2 + h) * F + j], a0[i], a1[i]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (q0 + i < S) {
+                        v0 += a0[i];
+                        v1 += a1[i];
+                    }
+            }
+        }
+        sm.p.red[0][h][jj] = v0;
+        sm.p.red[0][h][jj + 1] = v1;
+    }
+    __syncthreads();
+    for (int e = tid; e < CB / 2; e += kFT) {
+        const int jj = 2 * e, j = cb * CB + jj;
+        if (j < F) {
+            float sc[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float g = sm.p.red[0][0][jj + q], u = sm.p.red[0][1][jj + q];
+                if (QBITS == 8) {  // per-row scales
+                    g *= scales[j + q];
+                    u *= scales[F + j + q];
+                }
+                sc[q] = fabsf(silu(g) * u);
+            }
+            store_agent2(&score[j], sc[0], sc[1]);
+        }
+    }
+    if (!publish_and_ticket(&counters[kFusedScoreSlot], (uint32_t)n_cblocks, &sm.flag)) return;
+
+    // ---- 4. the last channel block: top-k over all F scores, every
+    // coherent load issued before any is used
+    if (k <= 0) return;
+    uint32_t fk[KF];
+#pragma unroll
+    for (int r = 0; r < KF; ++r) fk[r] = __float_as_uint(load_agent(&score[min(slot_index<KF>(r), F - 1)]));
+#pragma unroll
+    for (int r = 0; r < KF; ++r) fk[r] = (slot_index<KF>(r) < F) ? (fk[r] & 0x7FFFFFFFu) : 0u;
+    const SelectResult st = block_select<kFT, KF>(fk, F, k, sm.sel);
+    selection_bitmap<kFT, KF>(fk, F, st, sm.sel);
+    emit_bitmap<kFT>(F, sm.sel, [&](int i, uint32_t pos) {
+        if (pos < (uint32_t)k) sel[pos] = i;
+    });
+}
+
+// ------------------------------------------------------------------------
+FusedPlan fused_plan(int qbits, int64_t d, int64_t F)
+{
+    FusedPlan p;
+    const int cpl = qbits == 8 ? Fused<8>::CPL : Fused<4>::CPL;
+    const int rmax = qbits == 8 ? Fused<8>::RMAX : Fused<4>::RMAX;
+    const int gran = qbits == 8 ? Fused<8>::GRAN : Fused<4>::GRAN;
+    p.n_cblocks = (int)((F + 64 * cpl - 1) / (64 * cpl));
+    int s = kFusedSlots / p.n_cblocks;
+    if (s < 1) s = 1;
+    int R = (int)((d + s - 1) / s);
+    R = (R + gran - 1) / gran * gran;
+    if (R > rmax) R = rmax;
+    p.R = R;
+    p.S = (int)((d + R - 1) / R);
+    return p;
+}
+
+bool fused_supported(int64_t B, int64_t d, int64_t F) { return B == 1 && d <= kFusedMaxD && F <= kFusedMaxF; }
+
+hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
+                               const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
+                               uint32_t *counters, hipStream_t st)
+{
+    if (!fused_supported(1, d, F)) return hipErrorInvalidValue;
+    const FusedPlan pl = fused_plan(qbits, d, F);
+    const int kx = (d + kFT - 1) / kFT;
+    const int kf = (F + kFT - 1) / kFT;
+    const dim3 grid(pl.n_cblocks, pl.S);
+#define L1(T, Q, KXV, KFV)                                                                               \
+    stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k, codes, scales, \
+                                                             pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
+                                                             counters)
+#define L2(T, Q)                                       \
+    do {                                               \
+        if (kx <= 2 && kf <= 16) L1(T, Q, 2, 16);      \
+        else if (kx <= 2) L1(T, Q, 2, 32);             \
+        else if (kx <= 8 && kf <= 16) L1(T, Q, 8, 16); \
+        else if (kx <= 8) L1(T, Q, 8, 32);             \
+        else if (kf <= 16) L1(T, Q, 16, 16);           \
+        else L1(T, Q, 16, 32);                         \
+    } while (0)
+    if (dtype == 0) {
+        if (qbits == 8) L2(float, 8);
+        else L2(float, 4);
+    } else {
+        if (qbits == 8) L2(uint16_t, 8);
+        else L2(uint16_t, 4);
+    }
+#undef L2
+#undef L1
+    return hipGetLastError();
+}
+
+}  // namespace prox

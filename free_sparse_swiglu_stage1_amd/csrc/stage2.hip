@@ -84,7 +84,7 @@ __device__ __forceinline__ void stage_rows_f32(const T *__restrict__ x, int B, i
 }
 
 template <typename T, int NB>
-__global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d,
+__global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d, int F,
                                                      const T *__restrict__ w_gu, const int32_t *__restrict__ sel,
                                                      int k, float *__restrict__ s_sp, int32_t *__restrict__ iota_out)
 {
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int r = blockIdx.x * 4 + wv;  // one selected channel per wave
     const bool live = r < k;
-    const int j = live ? (sel ? sel[r] : r) : (sel ? sel[0] : 0);
+    const int j = (int)min((uint32_t)(live ? (sel ? sel[r] : r) : (sel ? sel[0] : 0)), (uint32_t)(F - 1));
     if (iota_out && live && lane == 0) iota_out[r] = r;
     const T *grow = w_gu + (int64_t)j * 2 * d;
     const T *urow = grow + d;
@@ -173,7 +173,7 @@ constexpr int kDownRowsPerWave = 16;
 template <typename T, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__ s_sp, int B, int k,
                                                        const T *__restrict__ wdt, const int32_t *__restrict__ sel,
-                                                       int d, int S, float *__restrict__ part,
+                                                       int d, int F, int S, float *__restrict__ part,
                                                        const T *residual, T *out, uint32_t *__restrict__ counters)
 {
     constexpr int NT = 64 * NW;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
     // lanes 0..15 fetch the channel index and s values of rank rw0 + lane
     const int rl = rw0 + (lane & (U - 1));
     const int rlc = rl < k ? rl : k - 1;
-    const int jl = sel ? sel[rlc] : rlc;
+    const int jl = (int)min((uint32_t)(sel ? sel[rlc] : rlc), (uint32_t)(F - 1));
     float sl_v[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) sl_v[b] = s_sp[(int64_t)(b < B ? b : 0) * k + rlc];
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *h, int d, float e
 // launchers
 // ------------------------------------------------------------------------
 template <typename T>
-static hipError_t gateup_t(const void *x, int B, int d, const void *w_gu, const int32_t *sel, int k, float *s_sp,
+static hipError_t gateup_t(const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel, int k, float *s_sp,
                            int32_t *iota_out, hipStream_t st)
 {
     if (k <= 0) return hipSuccess;
@@ -336,25 +336,26 @@ static hipError_t gateup_t(const void *x, int B, int d, const void *w_gu, const 
         float *sp = s_sp + (int64_t)b0 * k;
         int32_t *io = (b0 == 0) ? iota_out : nullptr;
         if (nb == 1)
-            gateup_kernel<T, 1><<<blocks, 256, d * sizeof(float), st>>>(xp, 1, d, (const T *)w_gu, sel, k, sp, io);
+            gateup_kernel<T, 1><<<blocks, 256, d * sizeof(float), st>>>(xp, 1, d, F, (const T *)w_gu, sel, k, sp, io);
         else
-            gateup_kernel<T, 4><<<blocks, 256, 4 * d * sizeof(float), st>>>(xp, nb, d, (const T *)w_gu, sel, k, sp, io);
+            gateup_kernel<T, 4><<<blocks, 256, 4 * d * sizeof(float), st>>>(xp, nb, d, F, (const T *)w_gu, sel, k, sp, io);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t launch_gateup(int dtype, const void *x, int B, int d, const void *w_gu, const int32_t *sel, int k,
-                         float *s_sp, int32_t *iota_out, hipStream_t st)
+hipError_t launch_gateup(int dtype, const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel,
+                         int k, float *s_sp, int32_t *iota_out, hipStream_t st)
 {
-    return dtype == 0 ? gateup_t<float>(x, B, d, w_gu, sel, k, s_sp, iota_out, st)
-                      : gateup_t<uint16_t>(x, B, d, w_gu, sel, k, s_sp, iota_out, st);
+    return dtype == 0 ? gateup_t<float>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, st)
+                      : gateup_t<uint16_t>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, st);
 }
 
 template <typename T>
 static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, const void *wdt, const int32_t *sel,
-                         int d, float *part, const void *residual, void *out, uint32_t *counters, hipStream_t st)
+                         int d, int F, float *part, const void *residual, void *out, uint32_t *counters,
+                         hipStream_t st)
 {
     dim3 grid(pl.n_slices, pl.S);
     dim3 grid4(pl.n_slices, 2 * pl.S);  // half-size workgroups for 4-token passes
@@ -365,10 +366,10 @@ static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, co
         const T *res = residual ? (const T *)residual + (int64_t)b0 * d : nullptr;
         T *o = (T *)out + (int64_t)b0 * d;
         if (nb == 1)
-            down_kernel<T, 1, kDownWaves><<<grid, 64 * kDownWaves, 0, st>>>(sp, 1, k, (const T *)wdt, sel, d, pl.S,
+            down_kernel<T, 1, kDownWaves><<<grid, 64 * kDownWaves, 0, st>>>(sp, 1, k, (const T *)wdt, sel, d, F, pl.S,
                                                                          part, res, o, counters);
         else
-            down_kernel<T, 4, kDownWaves / 2><<<grid4, 32 * kDownWaves, 0, st>>>(sp, nb, k, (const T *)wdt, sel, d,
+            down_kernel<T, 4, kDownWaves / 2><<<grid4, 32 * kDownWaves, 0, st>>>(sp, nb, k, (const T *)wdt, sel, d, F,
                                                                               2 * pl.S, part, res, o, counters);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -377,11 +378,11 @@ static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, co
 }
 
 hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
-                       const int32_t *sel, int d, float *part, const void *residual, void *out,
+                       const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st)
 {
-    return dtype == 0 ? down_t<float>(pl, s_sp, B, k, w_down_t, sel, d, part, residual, out, counters, st)
-                      : down_t<uint16_t>(pl, s_sp, B, k, w_down_t, sel, d, part, residual, out, counters, st);
+    return dtype == 0 ? down_t<float>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st)
+                      : down_t<uint16_t>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st);
 }
 
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st)

@@ -23,7 +23,7 @@ MODES = {"int8_row": Q_INT8_ROW, "int4_g128": Q_INT4_G128}
 
 SYMBOLS = (
     "prox_status_string", "prox_version", "prox_counts", "prox_pack_weights", "prox_proxy_sizes",
-    "prox_quantize_proxy", "prox_workspace_size", "prox_ffn_forward", "prox_ffn_forward_residual",
+    "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
 )
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         "prox_proxy_sizes": ([I64, I64, I32, PS, PS], I32),
         "prox_quantize_proxy": ([PW, I32, P, P, P], I32),
         "prox_workspace_size": ([I64, I64, I64, I32, PS], I32),
+        "prox_workspace_init": ([P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward": ([P, I64, PW, PP, F, F, P, P, P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward_residual": ([P, I64, PW, PP, F, F, P, P, P, P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward_timed": ([P, I64, PW, PP, F, F, P, P, P, ctypes.c_size_t, P, P], I32),
@@ -195,8 +196,16 @@ def workspace_size(d: int, F: int, batch: int, mode: str = "int8_row") -> int:
     return n.value
 
 
+def workspace_init(ws: torch.Tensor) -> torch.Tensor:
+    """Zero a workspace's ticket counters (once per allocation, before first use)."""
+    lib = load_library()
+    _check(lib.prox_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)), "prox_workspace_init")
+    return ws
+
+
 def alloc_workspace(d: int, F: int, batch: int, mode: str = "int8_row", device="cuda", extra: int = 0):
-    return torch.empty(workspace_size(d, F, batch, mode) + extra, dtype=torch.uint8, device=device)
+    ws = torch.empty(workspace_size(d, F, batch, mode) + extra, dtype=torch.uint8, device=device)
+    return workspace_init(ws)
 
 
 def _mode_name(p: Proxy) -> str:
@@ -318,8 +327,9 @@ def chain_forward(h: torch.Tensor, layers, proxies, input_keep: float, ffn_spars
     cws = (_CWeights * L)(*[w.c() for w in layers])
     cps = (_CProxy * L)(*[p.c() for p in proxies])
     if workspace is None:
-        workspace = torch.empty(chain_workspace_size(layers[0].d_model, layers[0].d_ff, B, _mode_name(proxies[0])),
-                                dtype=torch.uint8, device=h.device)
+        workspace = workspace_init(torch.empty(chain_workspace_size(layers[0].d_model, layers[0].d_ff, B,
+                                                                    _mode_name(proxies[0])),
+                                               dtype=torch.uint8, device=h.device))
     _check(lib.prox_chain_forward(_ptr(h), B, cws, cps, L, eps, input_keep, ffn_sparsity, _ptr(workspace),
                                   workspace.numel(), _stream(h.device)), "prox_chain_forward")
     return h

@@ -26,7 +26,9 @@
  *    8 <= d_model <= 16384, 16 <= d_ff <= 65520, 1 <= batch <= 16
  *    (int4-g128 proxy: batch <= 4); other sizes return PROX_ERR_UNSUPPORTED.
  *  - One workspace must not be used by two calls that may run concurrently.
- *    Its contents need no initialization and mean nothing between calls.
+ *    Its first 4096 bytes hold counters that must be zero before the
+ *    workspace's first use (prox_workspace_init, or any zero fill); every
+ *    call leaves them zero again.  The rest means nothing between calls.
  *
  * Notation: d = d_model, F = d_ff, B = batch, bf16 = bfloat16 bit patterns.
  */
@@ -132,6 +134,12 @@ prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *co
 prox_status prox_workspace_size(int64_t d_model, int64_t d_ff, int64_t batch, prox_qmode mode,
                                 size_t *bytes);
 
+/* Zero the counters of a workspace before its first use (enqueued on the
+ * stream).  workspace: device, workspace_bytes >= 4096.  Needed once per
+ * allocation, not per call: the cross-workgroup reductions elect their last
+ * workgroup with ticket counters that each call returns to zero. */
+prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The Prox FFN forward (both stages).
  *   x   [B][d] device, w->dtype: the FFN input (already normalized).
  *   out [B][d] device, w->dtype: y = sum over selected j of W_down[:, j] *
@@ -161,7 +169,9 @@ prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_w
  * selection, the proxy GEMV, the top-k, the gate/up GEMV and the down
  * projection, and after the down projection, so that hipEventElapsedTime of
  * consecutive pairs gives each step's duration on the device.  Without Stage 1
- * (k == 0 or k == F) events[1] and events[2] coincide. */
+ * (k == 0 or k == F) events[1] and events[2] coincide.  A single token with
+ * d <= 8192 and F <= 16384 runs all of Stage 1 as one kernel, between
+ * events[0] and events[1]; events[1] and events[2] then coincide. */
 prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w,
                                    const prox_proxy *p, float input_keep, float ffn_sparsity, void *out,
                                    int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
@@ -185,8 +195,9 @@ prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_id
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Stage 2 alone: exact masked SwiGLU on a given mask.
- *   sel_idx [k] device int32, distinct channels in [0, F) in ascending order;
- *   out [B][d] device.  0 <= k <= F. */
+ *   sel_idx [k] device int32, distinct channels in [0, F) in ascending order
+ *   (entries outside [0, F) are clamped into it: wrong values, no stray
+ *   access); out [B][d] device.  0 <= k <= F. */
 prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *w,
                               const int32_t *sel_idx, int64_t k, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
