@@ -8,11 +8,18 @@ each step streams its weights from HBM, not from the 256 MB Infinity Cache.
 
 Prints one JSON line: µs per layer (back-to-back steps on one stream), the
 layer's effective GB/s against the 8 TB/s HBM peak, the dominant kernel's
-roofline (measured live with HIP events around each kernel), the HIP-graph
-variant, and the CPU oracle timed on the host as a baseline.
+roofline, the HIP-graph variant, the dense (sparsity 0) comparator, and the
+CPU oracle timed on the host as a baseline.
+
+The dominant kernel's duration is measured live: a HIP graph of back-to-back
+launches of that kernel alone (cycling the weight sets) is replayed between
+two events on the stream it runs on, and the average per launch is taken.
 
     python bench.py [--steps K] [--warmup W] [--workload llama8b] [--batch 1]
-                    [--sparsity 0.7] [--mode int8_row] [--no-cpu]
+                    [--sparsity 0.7] [--mode int8_row] [--no-cpu] [--copy-calibration]
+
+--copy-calibration ends the run with a 256 MiB device-to-device copy, the
+known-size kernel against which the memory-traffic counters are scaled.
 """
 from __future__ import annotations
 
@@ -48,6 +55,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="weight copies cycled to defeat the Infinity Cache")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
@@ -61,9 +70,10 @@ def kept_union(x_f32: np.ndarray, k_in: int) -> int:
 
 
 def algorithmic_bytes(d, F, B, k, k_union, bw, mode):
-    """Bytes the method must move for one layer (SURVEY-style accounting):
-    x, proxy codes of the kept columns, proxy scales, the selected gate/up/down
-    rows, the mask, the output."""
+    """Bytes the method must move for one layer: x, proxy codes of the kept
+    columns (the union over tokens), proxy scales, the selected gate/up/down
+    rows, the mask, the output.  Workspace traffic (partials, scores) is not
+    counted."""
     if mode == "int8_row":
         proxy = 2 * k_union * F
         scales = 2 * F * 4
@@ -180,8 +190,12 @@ def main():
         for j, name in enumerate(P.STEP_NAMES):
             per[name].append(1000.0 * row[j].elapsed_time(row[j + 1]))
         lat.append(1000.0 * row[0].elapsed_time(row[5]))
-    kern_us = {n: statistics.mean(v) for n, v in per.items()}
-    kern_bytes = {"xselect": parts["x"], "proxy": parts["proxy"] + parts["scales"], "topk": F * 4 + k * 4,
+    step_us = {n: statistics.mean(v) for n, v in per.items()}
+    # Stage 1 is one kernel for a single token (the first mark pair brackets
+    # it); the marks themselves add a few µs each to what they bracket
+    stage1_us = step_us["xselect"] + step_us["proxy"] + step_us["topk"]
+    kern_us = {"stage1": stage1_us, "gateup": step_us["gateup"], "down": step_us["down"]}
+    kern_bytes = {"stage1": parts["x"] + parts["proxy"] + parts["scales"] + parts["sel"],
                   "gateup": parts["gateup"] + parts["x"] + 4 * B * k, "down": parts["down"] + parts["out"] + 4 * B * k}
     lat.sort()
     latency = dict(median=lat[len(lat) // 2], p10=lat[len(lat) // 10], p90=lat[(9 * len(lat)) // 10])
@@ -218,14 +232,61 @@ def main():
             print("graph capture unavailable: %r" % (exc,), file=sys.stderr)
     print("graph %s us/layer" % graph_us, file=sys.stderr, flush=True)
 
-    dom = "gateup"
-    dom_bytes = parts["gateup"]
-    dom_gbps = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
-    traffic = traffic_from_profiles(dom, args.workload)
+    # ---- the dominant kernel alone: a graph of back-to-back launches
+    dom = max(kern_us, key=kern_us.get)
+    dom_us, dom_kernel = kern_us[dom], None
+    if dom == "stage1":
+        dom_kernel = "stage1_fused_kernel" if B == 1 else "proxy_kernel"
+        sel_buf = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
+        n_l = 4 * R
+        try:
+            g1 = torch.cuda.CUDAGraph()
+            s1 = torch.cuda.Stream()
+            s1.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s1):
+                with torch.cuda.graph(g1, stream=s1):
+                    for i in range(n_l):
+                        w, p = sets[i % R]
+                        P.stage1_select(x, w, p, keep, sp, workspace=ws, sel_out=sel_buf)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g1.replay()
+            torch.cuda.synchronize()
+            n_rep = max(2, min(50, args.steps // n_l))
+            e0.record()
+            for _ in range(n_rep):
+                g1.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            dom_us = 1000.0 * e0.elapsed_time(e1) / (n_rep * n_l)
+        except Exception as exc:  # pragma: no cover
+            print("stage-1 graph timing unavailable (%r); using the marked step time" % (exc,), file=sys.stderr)
+    dom_bytes = kern_bytes[dom]
+    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    wl_name = "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s" % (args.workload, d, F, dtype, B, sp, keep, mode)
+    traffic = traffic_from_profiles(dom_kernel or dom, wl_name)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
-                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern_us[dom], 3)}
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom_kernel or dom,
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
     layer_gbps = layer_bytes / (us_layer * 1e-6) / 1e9
+
+    # ---- dense comparator: the same library at sparsity 0 (Stage 1 skipped)
+    dense_us = None
+    if not args.no_dense:
+        n_d = max(R, args.steps // 4)
+        for i in range(R):
+            w, p = sets[i % R]
+            P.ffn_forward(x, w, p, keep, 0.0, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n_d):
+            w, p = sets[i % R]
+            P.ffn_forward(x, w, p, keep, 0.0, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_us = 1000.0 * e0.elapsed_time(e1) / n_d
+    print("dominant %s %.2f us/launch; dense %s us/layer" % (dom_kernel or dom, dom_us, dense_us),
+          file=sys.stderr, flush=True)
 
     # ---- CPU oracle baseline (bounded sample on the host cores)
     cpu = None
@@ -271,7 +332,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s" % (args.workload, d, F, dtype, B, sp, keep, mode),
+        "config": {"workload": wl_name,
                    "d_model": d, "d_ff": F, "batch": B, "ffn_sparsity": sp, "input_keep": keep, "proxy": mode,
                    "k": k, "k_in": k_in, "kept_union": k_union, "weight_sets": R},
         "layer_bytes": layer_bytes,
@@ -282,10 +343,20 @@ def main():
         "kernels_us": {kk: round(v, 3) for kk, v in kern_us.items()},
         "kernels_gbps": {kk: round(kern_bytes[kk] / (kern_us[kk] * 1e-6) / 1e9, 1) for kk in kern_us},
         "roofline": roofline,
+        "dense_us_per_layer": None if dense_us is None else round(dense_us, 3),
         "cpu_baseline": cpu,
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+
+    if args.copy_calibration:  # known-size copy for the memory-traffic counters
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print("copy calibration: 3 device copies of %d bytes" % n, file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -118,7 +118,7 @@ DownPlan down_plan(int64_t d, int64_t k, int64_t B, prox_dtype t)
     p.vec = 16 / elem_bytes(t);
     p.cols = 64 * p.vec;
     p.n_slices = ceil_div(d, p.cols);
-    p.S = ceil_div(k > 0 ? k : 1, 16 * kDownWaves);  // 16 ranks per wave
+    p.S = ceil_div(k > 0 ? k : 1, kDownRowsPerWave * kDownWaves);
     p.nb = B >= 4 ? 4 : (int)B;
     return p;
 }
@@ -144,7 +144,7 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
         const FusedPlan fp = fused_plan(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
         if ((size_t)fp.S > part_rows) part_rows = fp.S;
     }
-    const int down_s_max = 2 * ceil_div(F, 16 * kDownWaves);  // 4-token passes use half-size workgroups
+    const int down_s_max = 2 * ceil_div(F, kDownRowsPerWave * kDownWaves);  // 4-token passes: half-size workgroups
     size_t off = 0;
     Workspace w;
     char *b = (char *)base;

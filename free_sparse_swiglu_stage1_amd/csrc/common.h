@@ -91,6 +91,33 @@ __device__ __forceinline__ void load_agent2(const float *p, float &a, float &b)
     b = __uint_as_float((uint32_t)(v >> 32));
 }
 
+// Batches of coherent loads whose count is only known at run time.  A load
+// under a branch is followed by a wait for it (the loads of a batch would
+// run one at a time), so the batch goes through a buffer resource instead:
+// every load is issued, and one whose offset is at or beyond the resource's
+// size reads as zero without a memory access.  The loads carry the same
+// device-scope coherence bit as the relaxed agent-scope atomic loads above.
+struct CoherentBuf {
+    static constexpr int kWord3 = 0x00020000;  // 32-bit data format, untyped access
+    static constexpr int kSc1 = 16;            // cache policy: device-scope coherent
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ __forceinline__ CoherentBuf(const void *base, uint32_t bytes)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kWord3))
+    {
+    }
+    // two floats at byte offset `off` (8-byte aligned)
+    __device__ __forceinline__ void load2(uint32_t off, float &a, float &b) const
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off, 0, kSc1);
+        a = __uint_as_float(v[0]);
+        b = __uint_as_float(v[1]);
+    }
+    __device__ __forceinline__ float load(uint32_t off) const
+    {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)off, 0, kSc1));
+    }
+};
+
 // All threads call after their store_agent()s.  Returns true in exactly one
 // workgroup of the `n` that share `counter`: the last to arrive, which then
 // resets the counter for the next use.

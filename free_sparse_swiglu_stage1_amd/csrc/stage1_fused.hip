@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     if (!publish_and_ticket(&counters[cb], (uint32_t)S, &sm.flag)) return;
 
     // ---- the last split of this channel block: scores of its channels
+    const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * 2 * F));
     for (int e = tid; e < CB; e += kFT) {
         const int h = e / (CB / 2), jj = 2 * (e % (CB / 2)), j = cb * CB + jj;
         float v0 = 0.0f, v1 = 0.0f;
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
             for (int q0 = 0; q0 < S; q0 += 16) {
                 float a0[16], a1[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    load_agent2(&part[((int64_t)min(q0 + i, S - 1) * 2 + h) * F + j], a0[i], a1[i]);
+                for (int i = 0; i < 16; ++i)  // splits >= S: beyond the buffer, read 0
+                    pbuf.load2((uint32_t)(sizeof(float) * ((min(q0 + i, S) * 2 + h) * F + j)), a0[i], a1[i]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (q0 + i < S) {

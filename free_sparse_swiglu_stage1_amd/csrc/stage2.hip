@@ -159,16 +159,15 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
 // ------------------------------------------------------------------------
 // K4: down projection over the selected rows of W_down^T [F][d].
 // Grid (column slices of 64*VEC outputs, S rank splits); a workgroup of
-// NW waves owns the ranks [s*16*NW, (s+1)*16*NW) of its slice, each wave 16
-// consecutive ranks, all 16 rows in flight at once: one vector load brings
-// the wave's 16 channel indices and s values, then the 16 row segments are
+// NW waves owns the ranks [s*U*NW, (s+1)*U*NW) of its slice, each wave U
+// consecutive ranks, all U rows in flight at once: one vector load brings
+// the wave's U channel indices and s values, then the U row segments are
 // loaded (16-byte loads, VEC columns per lane) and accumulated.  The waves
 // are combined in LDS in a fixed order into this split's partial; the last
-// split of a slice (atomic ticket) adds the partials -- the splits in NW
-// groups in parallel, each in split order, then the groups in order -- adds
-// the residual if any, rounds and stores.
+// split of a slice (atomic ticket) adds the partials -- interleaved groups
+// of splits in parallel, each group in split order, then the groups in
+// order -- adds the residual if any, rounds and stores.
 // ------------------------------------------------------------------------
-constexpr int kDownRowsPerWave = 16;
 
 template <typename T, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__ s_sp, int B, int k,
@@ -189,7 +188,7 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
     const int cc = active ? c : 0;
     const int rw0 = (s * NW + wv) * U;                    // this wave's first rank
     const int nr = max(0, min(U, k - rw0));               // ranks it holds (wave-uniform)
-    // lanes 0..15 fetch the channel index and s values of rank rw0 + lane
+    // lanes 0..U-1 fetch the channel index and s values of rank rw0 + lane
     const int rl = rw0 + (lane & (U - 1));
     const int rlc = rl < k ? rl : k - 1;
     const int jl = (int)min((uint32_t)(sel ? sel[rlc] : rlc), (uint32_t)(F - 1));
@@ -241,29 +240,32 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
         }
     }
     if (!publish_and_ticket(&counters[sl], (uint32_t)S, &s_last)) return;
-    // thread t: column pair t % (COLS/2), split group t / (COLS/2)
+    // thread t: column pair t % (COLS/2) of the splits grp, grp + GROUPS,
+    // grp + 2*GROUPS, ... (grp = t / (COLS/2)); every load is one this thread
+    // needs, issued before any is added (the predicate is wave-uniform)
     constexpr int PAIRS = COLS / 2;
     constexpr int GROUPS = NT / PAIRS;
-    constexpr int QB = 16;  // splits loaded per batch
+    constexpr int QMAX = 32;  // splits per thread the loads cover in one batch
     const int pair = tid % PAIRS, grp = tid / PAIRS;
     const int col0 = sl * COLS + pair * 2;
-    const int qa = (S * grp) / GROUPS, qe = (S * (grp + 1)) / GROUPS;
+    const int nq = (S - grp + GROUPS - 1) / GROUPS;  // this thread's splits
     float (*gsum)[NB][COLS] = reinterpret_cast<float (*)[NB][COLS]>(&red[0][0][0]);  // [GROUPS][NB][COLS]
     static_assert(GROUPS <= NW, "group sums must fit the reduction buffer");
     __syncthreads();
+    const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * B * d));
     for (int b = 0; b < NB; ++b) {
         float y0 = 0.0f, y1 = 0.0f;
-        if (b < B && col0 < d && qa < qe) {
-            for (int q0 = qa; q0 < qe; q0 += QB) {
-                float v0[QB], v1[QB];
+        if (b < B && col0 < d) {
+            for (int q0 = 0; q0 < nq; q0 += QMAX) {
+                float v0[QMAX], v1[QMAX];
 #pragma unroll
-                for (int i = 0; i < QB; ++i) {
-                    const int q = min(q0 + i, qe - 1);
-                    load_agent2(&part[((int64_t)q * B + b) * d + col0], v0[i], v1[i]);
+                for (int i = 0; i < QMAX; ++i) {  // past this thread's splits: beyond the buffer, reads 0
+                    const uint32_t q = (uint32_t)min(grp + (q0 + i) * GROUPS, S);
+                    pbuf.load2((uint32_t)(sizeof(float) * ((q * B + b) * d + col0)), v0[i], v1[i]);
                 }
 #pragma unroll
-                for (int i = 0; i < QB; ++i)
-                    if (q0 + i < qe) {
+                for (int i = 0; i < QMAX; ++i)
+                    if (q0 + i < nq) {
                         y0 += v0[i];
                         y1 += v1[i];
                     }

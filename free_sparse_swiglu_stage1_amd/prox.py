@@ -260,13 +260,13 @@ def ffn_forward_timed(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, 
 
 
 def stage1_select(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sparsity: float,
-                  with_scores: bool = False, workspace: torch.Tensor = None):
+                  with_scores: bool = False, workspace: torch.Tensor = None, sel_out: torch.Tensor = None):
     """Stage 1 alone: returns sel_idx (int32 [k], ascending) and, optionally, scores [F]."""
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
     _, k = counts(w.d_model, w.d_ff, input_keep, ffn_sparsity)
-    sel = torch.empty(max(k, 1), dtype=torch.int32, device=x.device)
+    sel = sel_out if sel_out is not None else torch.empty(max(k, 1), dtype=torch.int32, device=x.device)
     scores = torch.empty(w.d_ff, dtype=torch.float32, device=x.device) if with_scores else None
     if workspace is None:
         workspace = alloc_workspace(w.d_model, w.d_ff, B, _mode_name(p), x.device)

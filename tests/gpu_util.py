@@ -55,9 +55,15 @@ def unpack_proxy(p: P.Proxy):
 class Layer:
     """One seeded SwiGLU FFN layer on host (synth arrays) and device (packed)."""
 
-    def __init__(self, d, F, std, dtype, seed=0, layer=0):
+    def __init__(self, d, F, std, dtype, seed=0, layer=0, pattern=None):
         self.d, self.F, self.dtype = d, F, dtype
         self.wg, self.wu, self.wd = synth.make_weights(d, F, std, dtype, seed=seed, layer=layer)
+        if pattern == "dup":  # channel j + F/2 repeats channel j: every proxy score occurs twice
+            self.wg[F // 2:] = self.wg[:F // 2]
+            self.wu[F // 2:] = self.wu[:F // 2]
+        elif pattern == "zeros":  # 80% of the gate rows are zero: those channels score exactly 0
+            rng = np.random.default_rng(seed)
+            self.wg[rng.permutation(F)[: (4 * F) // 5]] = 0
         self.w = P.pack_weights(to_dev(self.wg), to_dev(self.wu), to_dev(self.wd))
         self._proxy = {}
         self._oproxy = {}

@@ -94,13 +94,28 @@ def test_topk_bit_exact(name, n, v):
 
 # -------------------------------------------------------------- stages
 
-@pytest.mark.parametrize("d,F,dtype,B,mode", [
-    (512, 1376, "f32", 1, "int8_row"), (1024, 2064, "bf16", 1, "int8_row"), (768, 1040, "bf16", 3, "int8_row"),
-    (1024, 1536, "bf16", 1, "int4_g128"), (640, 2000, "bf16", 4, "int4_g128"), (512, 784, "bf16", 16, "int8_row"),
+def _tied_x(B, d, dtype, seed):
+    """Inputs whose magnitudes take three values: input selection decides among ties."""
+    rng = np.random.default_rng(seed)
+    x = (rng.choice([0.5, 1.0, 2.0], size=(B, d)) * rng.choice([-1.0, 1.0], size=(B, d))).astype(np.float32)
+    return synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("d,F,dtype,B,mode,pattern", [
+    (512, 1376, "f32", 1, "int8_row", None), (1024, 2064, "bf16", 1, "int8_row", None),
+    (768, 1040, "bf16", 3, "int8_row", None), (1024, 1536, "bf16", 1, "int4_g128", None),
+    (640, 2000, "bf16", 4, "int4_g128", None), (512, 784, "bf16", 16, "int8_row", None),
+    # exact ties among the scores (duplicated channels) and at zero (zeroed gate rows),
+    # on the single-token kernel and on the batched path
+    (1024, 2064, "bf16", 1, "int8_row", "dup"), (1024, 1536, "bf16", 1, "int4_g128", "dup"),
+    (1024, 2064, "bf16", 1, "int8_row", "zeros"), (768, 1040, "bf16", 3, "int8_row", "zeros"),
+    # tied input magnitudes
+    (1024, 2064, "bf16", 1, "int8_row", "xties"), (2048, 4096, "f32", 1, "int8_row", "xties"),
+    (768, 1040, "bf16", 2, "int8_row", "xties"),
 ])
-def test_stage1_scores_and_mask(d, F, dtype, B, mode):
-    L = Layer(d, F, 0.02, dtype, seed=11)
-    xh = synth.make_x(B, d, dtype, seed=11)
+def test_stage1_scores_and_mask(d, F, dtype, B, mode, pattern):
+    L = Layer(d, F, 0.02, dtype, seed=11, pattern=pattern if pattern != "xties" else None)
+    xh = _tied_x(B, d, dtype, 11) if pattern == "xties" else synth.make_x(B, d, dtype, seed=11)
     sel, sc = P.stage1_select(to_dev(xh), L.w, L.proxy(mode), 0.5, 0.7, with_scores=True)
     torch.cuda.synchronize()
     ref = oracle.prox_forward(xh, L.wg, L.wu, L.wd, L.oracle_proxy(mode), 0.5, 0.7, mode)
