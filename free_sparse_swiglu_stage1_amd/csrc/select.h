@@ -196,6 +196,18 @@ __device__ SelectResult block_select(const uint32_t (&key)[KPT], int n, int k, S
     return radix_select_from<NT, KPT, MAXN>(key, n, all_and & known, known, (uint32_t)k, cursor, lowest, sm);
 }
 
+// The k-th largest of n keys when the bits outside [lowest, cursor] are known
+// to be zero in every key (sign-free keys: bit 31; keys of bf16 values: bits
+// 0..15), without first reducing the keys to find the window.
+template <int NT, int KPT, int MAXN>
+__device__ SelectResult block_select_window(const uint32_t (&key)[KPT], int n, int k, int cursor, int lowest,
+                                            SelectSmem<MAXN> &sm)
+{
+    uint32_t known = (cursor == 31) ? 0u : ~((2u << cursor) - 1u);
+    known |= (1u << lowest) - 1u;
+    return radix_select_from<NT, KPT, MAXN>(key, n, 0u, known, (uint32_t)k, cursor, lowest, sm);
+}
+
 // Keeps the lowest `keep` set bits of m.
 __device__ __forceinline__ uint32_t lowest_set_bits(uint32_t m, uint32_t keep)
 {
@@ -288,5 +300,25 @@ __device__ void emit_bitmap(int n, SelectSmem<MAXN> &sm, Emit emit)
 }
 
 __device__ __forceinline__ bool bitmap_test(const uint32_t *bits, int i) { return (bits[i >> 5] >> (i & 31)) & 1u; }
+
+// Index-order compaction: calls emit(i, pos) for every slot r of this thread
+// whose bit r of `mask` is set, pos its rank in index order among the set
+// bits of the block.  One ballot per row; a row's selected slots get
+// consecutive positions.
+template <int NT, int KPT, int MAXN, typename Emit>
+__device__ void emit_rows(uint64_t mask, SelectSmem<MAXN> &sm, Emit emit)
+{
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) cnt += (uint32_t)__popcll(__ballot((mask >> r) & 1ull));
+    uint32_t tot;
+    uint32_t pos = uniform_u32(waves_excl_scan<NT>(cnt, sm.scratch, &tot));
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const uint64_t m = __ballot((mask >> r) & 1ull);
+        if ((mask >> r) & 1ull) emit(slot_index<KPT>(r), pos + lanes_below(m));
+        pos += (uint32_t)__popcll(m);
+    }
+}
 
 }  // namespace prox

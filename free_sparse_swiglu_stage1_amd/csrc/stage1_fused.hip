@@ -116,23 +116,47 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
         if (slot_index<KX>(r) >= d) xv[r] = 0.0f;
         key[r] = __float_as_uint(xv[r]) & 0x7FFFFFFFu;
     }
-    const SelectResult sr = block_select<kFT, KX>(key, d, k_in, sm.sel);
-    selection_bitmap<kFT, KX>(key, d, sr, sm.sel);
-    int nk = 0;  // the split's kept inputs, listed in ascending order
+    // keys of bf16 values have 16 zero low bits
+    const SelectResult sr = block_select_window<kFT, KX>(key, d, k_in, 30, sizeof(T) == 2 ? 16 : 0, sm.sel);
+    const uint32_t T_x = uniform_u32(sr.T), need_eq = uniform_u32(sr.need_eq);
+    const bool all_eq = need_eq == uniform_u32(sr.count_eq);
+    // keys equal to T_x: the need_eq of lowest index are kept; avail of them
+    // are left for this split once those before it are counted
+    uint32_t avail = need_eq;
+    if (!all_eq) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < KX; ++r)
+            c += (uint32_t)__popcll(__ballot((slot_index<KX>(r) < i0) & (key[r] == T_x)));
+        uint32_t before_tot;
+        (void)waves_excl_scan<kFT>(c, sm.sel.scratch, &before_tot);
+        before_tot = uniform_u32(before_tot);
+        avail = need_eq > before_tot ? need_eq - before_tot : 0u;
+    }
+    // the split's kept inputs, listed in ascending order: one scan of packed
+    // (greater, equal) counts gives every position
+    uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
     for (int q = 0; q < XR; ++q) {
         if (q * kFT >= R) break;  // uniform
         const int i = i0 + q * kFT + tid;
-        const bool kept = i < i1 && bitmap_test(sm.sel.bits, i);
-        const uint64_t m = __ballot(kept);
+        const uint32_t kk = __float_as_uint(xr[q]) & 0x7FFFFFFFu;
+        const bool in = i < i1;
+        const bool gt = in && (all_eq ? kk >= T_x : kk > T_x);
+        const bool eq = in && !all_eq && kk == T_x;
+        const uint32_t v = (gt ? 1u : 0u) | (eq ? 0x10000u : 0u);
         uint32_t tot;
-        const uint32_t before = uniform_u32(waves_excl_scan<kFT>((uint32_t)__popcll(m), sm.sel.scratch, &tot));
-        if (kept) {
-            sm.li[nk + before + lanes_below(m)] = i;
-            sm.lx[nk + before + lanes_below(m)] = xr[q];
+        const uint32_t before = block_excl_scan<kFT>(v, sm.sel.scratch, &tot);
+        const uint32_t gt_before = n_gt + (before & 0xFFFFu), eq_before = n_eq + (before >> 16);
+        if (gt || (eq && eq_before < avail)) {
+            const uint32_t pos = gt_before + min(eq_before, avail);
+            sm.li[pos] = i;
+            sm.lx[pos] = xr[q];
         }
-        nk += (int)uniform_u32(tot);
+        n_gt += uniform_u32(tot) & 0xFFFFu;
+        n_eq += uniform_u32(tot) >> 16;
     }
+    const int nk = (int)(n_gt + min(n_eq, avail));
     if (QBITS == 4) {
 #pragma unroll
         for (int q = 0; q < GS; ++q) {
@@ -269,11 +293,21 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     for (int r = 0; r < KF; ++r) fk[r] = __float_as_uint(load_agent(&score[min(slot_index<KF>(r), F - 1)]));
 #pragma unroll
     for (int r = 0; r < KF; ++r) fk[r] = (slot_index<KF>(r) < F) ? (fk[r] & 0x7FFFFFFFu) : 0u;
-    const SelectResult st = block_select<kFT, KF>(fk, F, k, sm.sel);
-    selection_bitmap<kFT, KF>(fk, F, st, sm.sel);
-    emit_bitmap<kFT>(F, sm.sel, [&](int i, uint32_t pos) {
+    // scores are sign-free: the window is bits 30..0
+    const SelectResult st = block_select_window<kFT, KF>(fk, F, k, 30, 0, sm.sel);
+    auto put = [&](int i, uint32_t pos) {
         if (pos < (uint32_t)k) sel[pos] = i;
-    });
+    };
+    if (uniform_u32(st.need_eq) == uniform_u32(st.count_eq)) {  // no tie to break: key >= T
+        const uint32_t T_s = uniform_u32(st.T);
+        uint64_t chosen = 0;
+#pragma unroll
+        for (int r = 0; r < KF; ++r) chosen |= (uint64_t)((slot_index<KF>(r) < F) & (fk[r] >= T_s)) << r;
+        emit_rows<kFT, KF>(chosen, sm.sel, put);
+    } else {
+        selection_bitmap<kFT, KF>(fk, F, st, sm.sel);
+        emit_bitmap<kFT>(F, sm.sel, put);
+    }
 }
 
 // ------------------------------------------------------------------------
