@@ -14,11 +14,16 @@ namespace {
 
 constexpr int kMaxBatch = 16;
 constexpr int kMaxBatchInt4 = 4;
-// The workspace starts with ticket counters that must be zero between
-// calls: [0,511) proxy channel blocks, 511 the single-token Stage 1's score
-// ticket, [512,1024) down slices.  Each is reset by its last arriver.
-constexpr int kCounters = 1024;
+// The workspace starts with counters that must be zero between calls:
+// [0,511) proxy channel blocks, 511 the single-token Stage 1's score ticket,
+// [512,576) down slices, 1023 a wait-timeout flag, then from 4096 the
+// single-token Stage 2's per-split lines (64 pages of 4 KB).  Each is reset
+// by the last workgroup to use it.
+constexpr int kCounters = kS2SyncBase + kS2SyncWords;
 constexpr int kZeroWords = kCounters;
+// The ticket words and the timeout flag: what a call clears on entry where it
+// does not rely on the previous call having left them zero.
+constexpr int kTicketWords = kS2TimeoutSlot + 1;
 constexpr int kTargetProxyBlocks = 1024;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -189,7 +194,7 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
     const ProxyPlan pp = proxy_plan(d, F, B, p->mode);
     TRY_HIP(mark(ev, 0, st));
     TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
-                           kCounters, st));
+                           kTicketWords, st));
     TRY_HIP(mark(ev, 1, st));
     TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes, (const float *)p->scales,
                          ws.proxy_part, score, ws.counters, st));
@@ -211,11 +216,17 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
+    if (B == 1) {  // one launch: the down projection starts while gate/up drains
+        TRY_HIP(launch_stage2_fused(dt, x, (int)d, (int)w->d_ff, w->w_gu, w->w_down_t, sel, (int)k, ws.s_sp,
+                                    ws.down_part, residual, out, ws.counters, iota_out, st));
+        TRY_HIP(mark(ev, 4, st));
+        return hip_status(mark(ev, 5, st));
+    }
     TRY_HIP(launch_gateup(dt, x, (int)B, (int)d, (int)w->d_ff, w->w_gu, sel, (int)k, ws.s_sp, iota_out, st));
     TRY_HIP(mark(ev, 4, st));
     const DownPlan dp = down_plan(d, k, B, w->dtype);
     TRY_HIP(launch_down(dt, dp, ws.s_sp, (int)B, (int)k, w->w_down_t, sel, (int)d, (int)w->d_ff, ws.down_part, residual, out,
-                        ws.counters + 512, st));
+                        ws.counters + kDownSliceBase, st));
     return hip_status(mark(ev, 5, st));
 }
 
@@ -240,7 +251,7 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     const int64_t F = w->d_ff;
     if (k == 0 || k == F) {  // no Stage 1
         TRY_HIP(mark(ev, 0, st));
-        TRY_HIP(launch_zero_u32(ws.counters, kCounters, st));
+        TRY_HIP(launch_zero_u32(ws.counters, kTicketWords, st));
         TRY_HIP(mark(ev, 1, st));
         TRY_HIP(mark(ev, 2, st));
         return run_stage2(x, B, w, nullptr, k, residual, out, k ? sel_out : nullptr, ws, st, ev);
@@ -407,7 +418,7 @@ prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *
     if (x == out) return PROX_ERR_INVALID_ARG;
     const Workspace ws = layout(w->d_model, w->d_ff, batch, PROX_Q_INT8_ROW, workspace);
     if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
-    TRY_HIP(launch_zero_u32(ws.counters, kCounters, stream));
+    TRY_HIP(launch_zero_u32(ws.counters, kTicketWords, stream));
     return run_stage2(x, batch, w, sel_idx, k, nullptr, out, nullptr, ws, stream);
 }
 

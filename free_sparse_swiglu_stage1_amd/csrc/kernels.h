@@ -67,6 +67,28 @@ hipError_t launch_gateup(int dtype, const void *x, int B, int d, int F, const vo
 hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
+// Stage 2 for one token in one launch (stage2.hip).  Counter slots:
+// [kDownSliceBase, +64) slice tickets, kS2TimeoutSlot a wait timeout, and
+// from kS2SyncBase one 128-byte line per split (its readiness count, then its
+// count of down workgroups past the wait).  Split s sits in 4 KB page s % 64,
+// line s / 64: the lines being polled at one time are 4 KB apart, so the
+// polls spread over the memory channels instead of queueing on one (one
+// packed run of counters slowed every gate/up row on that channel about 3x).
+constexpr int kDownSliceBase = 512;
+constexpr int kS2TimeoutSlot = 1023;
+constexpr int kS2SyncBase = 4096;
+constexpr int kS2SyncPages = 64;
+constexpr int kS2PageWords = 1024;
+constexpr int kS2LineWords = 32;
+constexpr int kS2MaxSplits = kS2SyncPages * (kS2PageWords / kS2LineWords);
+constexpr int kS2SyncWords = kS2SyncPages * kS2PageWords;
+__host__ __device__ constexpr int s2_sync_line(int s)
+{
+    return kS2SyncBase + (s % kS2SyncPages) * kS2PageWords + (s / kS2SyncPages) * kS2LineWords;
+}
+hipError_t launch_stage2_fused(int dtype, const void *x, int d, int F, const void *w_gu, const void *w_down_t,
+                               const int32_t *sel, int k, float *s_sp, float *part, const void *residual, void *out,
+                               uint32_t *counters, int32_t *iota_out, hipStream_t st);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
 

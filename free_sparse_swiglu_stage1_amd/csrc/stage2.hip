@@ -83,16 +83,20 @@ __device__ __forceinline__ void stage_rows_f32(const T *__restrict__ x, int B, i
     __syncthreads();
 }
 
-template <typename T, int NB>
-__global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d, int F,
-                                                     const T *__restrict__ w_gu, const int32_t *__restrict__ sel,
-                                                     int k, float *__restrict__ s_sp, int32_t *__restrict__ iota_out)
+// One gate/up workgroup (4 waves, one selected channel each: ranks
+// 4 blk .. 4 blk + 3).  xs: LDS for x as fp32, [NB][d].  COHERENT: s is stored with
+// device-coherent stores, for other workgroups of the same launch.
+template <typename T, int NB, bool COHERENT>
+__device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int d, int F,
+                                             const T *__restrict__ w_gu, const int32_t *__restrict__ sel, int k,
+                                             float *__restrict__ s_sp, int32_t *__restrict__ iota_out, float *xs,
+                                             int blk)
 {
     constexpr int V = vec16<T>::N;  // elements per 16-byte load
     constexpr int UNR = 8;          // 16-byte vectors per lane per pass (two rows: 2*UNR loads)
-    extern __shared__ float xs[];   // [NB][d]
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
-    const int r = blockIdx.x * 4 + wv;  // one selected channel per wave
+    (void)tid;
+    const int r = blk * 4 + wv;  // one selected channel per wave
     const bool live = r < k;
     const int j = (int)min((uint32_t)(live ? (sel ? sel[r] : r) : (sel ? sel[0] : 0)), (uint32_t)(F - 1));
     if (iota_out && live && lane == 0) iota_out[r] = r;
@@ -152,8 +156,22 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
     for (int b = 0; b < NB; ++b) {
         const float g = wave_sum(ag[b]);
         const float u = wave_sum(au[b]);
-        if (live && lane == 0 && b < B) s_sp[(int64_t)b * k + r] = silu(g) * u;
+        if (live && lane == 0 && b < B) {
+            if (COHERENT)
+                store_agent(&s_sp[(int64_t)b * k + r], silu(g) * u);
+            else
+                s_sp[(int64_t)b * k + r] = silu(g) * u;
+        }
     }
+}
+
+template <typename T, int NB>
+__global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d, int F,
+                                                     const T *__restrict__ w_gu, const int32_t *__restrict__ sel,
+                                                     int k, float *__restrict__ s_sp, int32_t *__restrict__ iota_out)
+{
+    extern __shared__ float xs[];  // [NB][d]
+    gateup_block<T, NB, false>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, xs, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------
@@ -168,6 +186,85 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
 // of splits in parallel, each group in split order, then the groups in
 // order -- adds the residual if any, rounds and stores.
 // ------------------------------------------------------------------------
+
+// The end of a down-projection workgroup: its waves' accumulators are added
+// in LDS in wave order into this split's partial (coherent 64-bit stores);
+// the last split of the slice to finish (ticket) adds the partials --
+// interleaved groups of splits in parallel, each group in split order, then
+// the groups in order -- adds the residual if any, rounds and stores.
+template <typename T, int NB, int NW>
+__device__ __forceinline__ void down_finish(const float (&acc)[NB][vec16<T>::N],
+                                            float (&red)[NW][NB][64 * vec16<T>::N], int *s_last, int sl, int s,
+                                            int B, int d, int S, float *__restrict__ part, const T *residual,
+                                            T *out, uint32_t *slice_counter)
+{
+    constexpr int NT = 64 * NW;
+    constexpr int V = vec16<T>::N;
+    constexpr int COLS = 64 * V;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < V; ++q) red[wv][b][lane * V + q] = acc[b][q];
+    __syncthreads();
+    for (int e = tid; e < NB * COLS / 2; e += NT) {  // column pairs
+        const int b = e / (COLS / 2), ci = 2 * (e % (COLS / 2)), col = sl * COLS + ci;
+        if (b < B && col < d) {
+            float v0 = red[0][b][ci], v1 = red[0][b][ci + 1];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                v0 += red[w][b][ci];
+                v1 += red[w][b][ci + 1];
+            }
+            store_agent2(&part[((int64_t)s * B + b) * d + col], v0, v1);
+        }
+    }
+    if (!publish_and_ticket(slice_counter, (uint32_t)S, s_last)) return;
+    // thread t: column pair t % (COLS/2) of the splits grp, grp + GROUPS,
+    // grp + 2*GROUPS, ... (grp = t / (COLS/2)); every load is one this thread
+    // needs, issued before any is added (the predicate is wave-uniform)
+    constexpr int PAIRS = COLS / 2;
+    constexpr int GROUPS = NT / PAIRS;
+    constexpr int QMAX = 36;  // splits per thread the loads cover in one batch (S <= 72: two batches)
+    const int pair = tid % PAIRS, grp = tid / PAIRS;
+    const int col0 = sl * COLS + pair * 2;
+    const int nq = (S - grp + GROUPS - 1) / GROUPS;  // this thread's splits
+    float (*gsum)[NB][COLS] = reinterpret_cast<float (*)[NB][COLS]>(&red[0][0][0]);  // [GROUPS][NB][COLS]
+    static_assert(GROUPS <= NW, "group sums must fit the reduction buffer");
+    __syncthreads();
+    const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * B * d));
+    for (int b = 0; b < NB; ++b) {
+        float y0 = 0.0f, y1 = 0.0f;
+        if (b < B && col0 < d) {
+            for (int q0 = 0; q0 < nq; q0 += QMAX) {
+                float v0[QMAX], v1[QMAX];
+#pragma unroll
+                for (int i = 0; i < QMAX; ++i) {  // past this thread's splits: beyond the buffer, reads 0
+                    const uint32_t q = (uint32_t)min(grp + (q0 + i) * GROUPS, S);
+                    pbuf.load2((uint32_t)(sizeof(float) * ((q * B + b) * d + col0)), v0[i], v1[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < QMAX; ++i)
+                    if (q0 + i < nq) {
+                        y0 += v0[i];
+                        y1 += v1[i];
+                    }
+            }
+        }
+        gsum[grp][b][pair * 2] = y0;
+        gsum[grp][b][pair * 2 + 1] = y1;
+    }
+    __syncthreads();
+    for (int e = tid; e < B * COLS; e += NT) {
+        const int b = e / COLS, ci = e % COLS, col = sl * COLS + ci;
+        if (col >= d || b >= NB) continue;
+        float y = gsum[0][b][ci];
+#pragma unroll
+        for (int g = 1; g < GROUPS; ++g) y += gsum[g][b][ci];
+        if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
+        elem<T>::store(out, (int64_t)b * d + col, y);
+    }
+}
 
 template <typename T, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__ s_sp, int B, int k,
@@ -222,68 +319,115 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
         }
     }
 
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int q = 0; q < V; ++q) red[wv][b][lane * V + q] = acc[b][q];
-    __syncthreads();
-    for (int e = tid; e < NB * COLS / 2; e += NT) {  // column pairs
-        const int b = e / (COLS / 2), ci = 2 * (e % (COLS / 2)), col = sl * COLS + ci;
-        if (b < B && col < d) {
-            float v0 = red[0][b][ci], v1 = red[0][b][ci + 1];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                v0 += red[w][b][ci];
-                v1 += red[w][b][ci + 1];
-            }
-            store_agent2(&part[((int64_t)s * B + b) * d + col], v0, v1);
+    down_finish<T, NB, NW>(acc, red, &s_last, sl, s, B, d, S, part, residual, out, &counters[sl]);
+}
+
+// ------------------------------------------------------------------------
+// K3 + K4 for one token in one launch, so that the down projection's start
+// overlaps the gate/up tail instead of following a kernel boundary.
+//
+// Workgroups [0, n_gu) are gate/up workgroups (gateup_block, s stored
+// device-coherently) that count themselves done in their split's readiness
+// counter (its own 128-byte line, s2_sync_line); a split is
+// 64 ranks, i.e. 16 gate/up workgroups.  Workgroups [n_gu, n_gu + n_down) are
+// down workgroups (slice, split): each waits until the 16 gate/up workgroups
+// of its split are done, then streams its 64 rows (4 waves x 16 rows, all in
+// flight) and ends as down_kernel does.  Waiting before loading keeps the
+// down rows out of the memory queue while the gate/up rows drain.
+//
+// Workgroups are dispatched in index order on every XCD, so every gate/up
+// workgroup has been dispatched before any down workgroup waits, and gate/up
+// workgroups wait for nothing.  The wait is bounded in time all the same (a
+// timeout sets counters[kS2TimeoutSlot] and the workgroup goes on); the last
+// down workgroup of a split to pass the wait resets its counters.
+// ------------------------------------------------------------------------
+constexpr int kS2Waves = 4;
+constexpr int kS2Rows = 16;                           // down rows per wave, all in flight
+constexpr int kS2Ranks = kS2Waves * kS2Rows;          // ranks per split
+constexpr int kS2GuPerSplit = kS2Ranks / 4;           // gate/up workgroups (4 ranks each) per split
+constexpr uint64_t kSpinTicks = 50000000ull;          // 0.5 s of the 100 MHz real-time counter
+
+// thread 0 only: waits until *ctr >= target; false on timeout
+__device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(8);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
+    }
+    return true;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
+    const T *__restrict__ x, int d, int F, const T *__restrict__ w_gu, const T *__restrict__ wdt,
+    const int32_t *__restrict__ sel, int k, int n_gu, int n_slices, int S, float *__restrict__ s_sp,
+    float *__restrict__ part, const T *residual, T *out, uint32_t *__restrict__ counters,
+    int32_t *__restrict__ iota_out)
+{
+    constexpr int V = vec16<T>::N;
+    constexpr int COLS = 64 * V;
+    extern __shared__ float dyn[];  // gate/up: x [d]; down: red [kS2Waves][1][COLS]
+    __shared__ int s_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+
+    if ((int)blockIdx.x < n_gu) {
+        gateup_block<T, 1, true>(x, 1, d, F, w_gu, sel, k, s_sp, iota_out, dyn, blockIdx.x);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's s stores have completed
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(&counters[s2_sync_line(blockIdx.x / kS2GuPerSplit)], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    // ---- down: (slice sl, split s) over ranks [64 s, 64 s + 64)
+    const int dw = (int)blockIdx.x - n_gu;
+    const int sl = dw % n_slices, s = dw / n_slices;
+    if (tid == 0) {
+        uint32_t *ready = &counters[s2_sync_line(s)], *consumed = ready + 16;
+        const int r_end = min(k, (s + 1) * kS2Ranks);
+        const uint32_t target = (uint32_t)((r_end + 3) / 4 - s * kS2GuPerSplit);
+        if (!spin_wait_geq(ready, target))
+            __hip_atomic_store(&counters[kS2TimeoutSlot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__hip_atomic_fetch_add(consumed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)n_slices - 1) {  // every down workgroup of the split has passed the wait
+            __hip_atomic_store(ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(consumed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (!publish_and_ticket(&counters[sl], (uint32_t)S, &s_last)) return;
-    // thread t: column pair t % (COLS/2) of the splits grp, grp + GROUPS,
-    // grp + 2*GROUPS, ... (grp = t / (COLS/2)); every load is one this thread
-    // needs, issued before any is added (the predicate is wave-uniform)
-    constexpr int PAIRS = COLS / 2;
-    constexpr int GROUPS = NT / PAIRS;
-    constexpr int QMAX = 32;  // splits per thread the loads cover in one batch
-    const int pair = tid % PAIRS, grp = tid / PAIRS;
-    const int col0 = sl * COLS + pair * 2;
-    const int nq = (S - grp + GROUPS - 1) / GROUPS;  // this thread's splits
-    float (*gsum)[NB][COLS] = reinterpret_cast<float (*)[NB][COLS]>(&red[0][0][0]);  // [GROUPS][NB][COLS]
-    static_assert(GROUPS <= NW, "group sums must fit the reduction buffer");
     __syncthreads();
-    const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * B * d));
-    for (int b = 0; b < NB; ++b) {
-        float y0 = 0.0f, y1 = 0.0f;
-        if (b < B && col0 < d) {
-            for (int q0 = 0; q0 < nq; q0 += QMAX) {
-                float v0[QMAX], v1[QMAX];
+    const int c = sl * COLS + lane * V;
+    const int cc = c < d ? c : 0;
+    const int rw0 = (s * kS2Waves + wv) * kS2Rows;  // this wave's first rank
+    const int nr = max(0, min(kS2Rows, k - rw0));    // ranks it holds (wave-uniform)
+    const int rl = rw0 + (lane & (kS2Rows - 1));
+    const int rlc = rl < k ? rl : k - 1;
+    const int jl = (int)min((uint32_t)(sel ? sel[rlc] : rlc), (uint32_t)(F - 1));
+    const float sv_l = load_agent(&s_sp[rlc]);
+    float acc[1][V];
 #pragma unroll
-                for (int i = 0; i < QMAX; ++i) {  // past this thread's splits: beyond the buffer, reads 0
-                    const uint32_t q = (uint32_t)min(grp + (q0 + i) * GROUPS, S);
-                    pbuf.load2((uint32_t)(sizeof(float) * ((q * B + b) * d + col0)), v0[i], v1[i]);
-                }
+    for (int q = 0; q < V; ++q) acc[0][q] = 0.0f;
+    if (nr > 0) {
+        u32x4 w[kS2Rows];
 #pragma unroll
-                for (int i = 0; i < QMAX; ++i)
-                    if (q0 + i < nq) {
-                        y0 += v0[i];
-                        y1 += v1[i];
-                    }
+        for (int u = 0; u < kS2Rows; ++u) {
+            const int j = __builtin_amdgcn_readlane(jl, u);
+            if (u < nr) w[u] = ld_stream(wdt + (int64_t)j * d + cc);
+        }
+#pragma unroll
+        for (int u = 0; u < kS2Rows; ++u) {
+            if (u < nr) {
+                float f[V];
+                vec16<T>::unpack(w[u], f);
+                const float sv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_l), u));
+#pragma unroll
+                for (int q = 0; q < V; ++q) acc[0][q] = fmaf(sv, f[q], acc[0][q]);
             }
         }
-        gsum[grp][b][pair * 2] = y0;
-        gsum[grp][b][pair * 2 + 1] = y1;
     }
-    __syncthreads();
-    for (int e = tid; e < B * COLS; e += NT) {
-        const int b = e / COLS, ci = e % COLS, col = sl * COLS + ci;
-        if (col >= d || b >= NB) continue;
-        float y = gsum[0][b][ci];
-#pragma unroll
-        for (int g = 1; g < GROUPS; ++g) y += gsum[g][b][ci];
-        if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
-        elem<T>::store(out, (int64_t)b * d + col, y);
-    }
+    down_finish<T, 1, kS2Waves>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d, S,
+                                part, residual, out, &counters[kDownSliceBase + sl]);
 }
 
 // out = residual (or 0): the k == 0 case
@@ -385,6 +529,29 @@ hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, 
 {
     return dtype == 0 ? down_t<float>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st)
                       : down_t<uint16_t>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st);
+}
+
+hipError_t launch_stage2_fused(int dtype, const void *x, int d, int F, const void *w_gu, const void *w_down_t,
+                               const int32_t *sel, int k, float *s_sp, float *part, const void *residual, void *out,
+                               uint32_t *counters, int32_t *iota_out, hipStream_t st)
+{
+    if (k <= 0) return hipErrorInvalidValue;
+    const int V = dtype == 0 ? 4 : 8;
+    const int n_gu = (k + 3) / 4;
+    const int n_slices = (d + 64 * V - 1) / (64 * V);
+    const int S = (k + kS2Ranks - 1) / kS2Ranks;
+    if (S > kS2MaxSplits || n_slices > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
+    const dim3 grid(n_gu + n_slices * S);
+    const size_t lds = sizeof(float) * (size_t)max(d, kS2Waves * 64 * V);
+    if (dtype == 0)
+        stage2_fused_kernel<float><<<grid, 64 * kS2Waves, lds, st>>>(
+            (const float *)x, d, F, (const float *)w_gu, (const float *)w_down_t, sel, k, n_gu, n_slices, S, s_sp,
+            part, (const float *)residual, (float *)out, counters, iota_out);
+    else
+        stage2_fused_kernel<uint16_t><<<grid, 64 * kS2Waves, lds, st>>>(
+            (const uint16_t *)x, d, F, (const uint16_t *)w_gu, (const uint16_t *)w_down_t, sel, k, n_gu, n_slices, S,
+            s_sp, part, (const uint16_t *)residual, (uint16_t *)out, counters, iota_out);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st)

@@ -26,7 +26,7 @@
  *    8 <= d_model <= 16384, 16 <= d_ff <= 65520, 1 <= batch <= 16
  *    (int4-g128 proxy: batch <= 4); other sizes return PROX_ERR_UNSUPPORTED.
  *  - One workspace must not be used by two calls that may run concurrently.
- *    Its first 4096 bytes hold counters that must be zero before the
+ *    Its first 278528 bytes hold counters that must be zero before the
  *    workspace's first use (prox_workspace_init, or any zero fill); every
  *    call leaves them zero again.  The rest means nothing between calls.
  *
@@ -135,7 +135,7 @@ prox_status prox_workspace_size(int64_t d_model, int64_t d_ff, int64_t batch, pr
                                 size_t *bytes);
 
 /* Zero the counters of a workspace before its first use (enqueued on the
- * stream).  workspace: device, workspace_bytes >= 4096.  Needed once per
+ * stream).  workspace: device, workspace_bytes >= 278528.  Needed once per
  * allocation, not per call: the cross-workgroup reductions elect their last
  * workgroup with ticket counters that each call returns to zero. */
 prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -171,7 +171,9 @@ prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_w
  * consecutive pairs gives each step's duration on the device.  Without Stage 1
  * (k == 0 or k == F) events[1] and events[2] coincide.  A single token with
  * d <= 8192 and F <= 16384 runs all of Stage 1 as one kernel, between
- * events[0] and events[1]; events[1] and events[2] then coincide. */
+ * events[0] and events[1]; events[1] and events[2] then coincide.  A single
+ * token runs all of Stage 2 as one kernel, between events[3] and events[4];
+ * events[4] and events[5] then coincide. */
 prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w,
                                    const prox_proxy *p, float input_keep, float ffn_sparsity, void *out,
                                    int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,

@@ -226,3 +226,28 @@ def test_workspace_reuse_across_shapes():
         fresh = P.ffn_forward(xt, L.w, L.proxy("int8_row"), 0.5, sp)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), (B, sp)
+
+
+COUNTER_BYTES = 278528  # the workspace's leading counter block (include/prox.h)
+
+
+def test_counters_left_zero():
+    # every call hands the workspace back with its counters at zero: the
+    # single-token kernels' tickets, per-split readiness lines and timeout flag
+    L = Layer(1024, 4096, 0.02, "bf16", seed=41)
+    n1, n3 = P.workspace_size(1024, 4096, 1), P.workspace_size(1024, 4096, 3)
+    ws = P.alloc_workspace(1024, 4096, 3, extra=max(0, n1 - n3))  # serves B = 1 and B = 3
+
+    def nonzero():
+        torch.cuda.synchronize()
+        return int(torch.count_nonzero(ws[:COUNTER_BYTES]).item())
+
+    assert nonzero() == 0
+    for B, sp in ((1, 0.7), (1, 0.33), (1, 0.93), (3, 0.7), (1, 0.0), (1, 0.7)):
+        x = to_dev(synth.make_x(B, 1024, "bf16", seed=50 + B))
+        P.ffn_forward(x, L.w, L.proxy("int8_row"), 0.5, sp, workspace=ws)
+        assert nonzero() == 0, (B, sp)
+    x = to_dev(synth.make_x(1, 1024, "bf16", seed=60))
+    sel = torch.arange(0, 4096, 3, dtype=torch.int32, device="cuda")  # k = 1366: a ragged last split
+    P.stage2_exact(x, L.w, sel, workspace=ws)
+    assert nonzero() == 0
