@@ -118,6 +118,22 @@ struct CoherentBuf {
     }
 };
 
+// Plain 32-bit stores through a buffer resource of `bytes` bytes: a store at
+// an offset >= bytes is dropped by the hardware's range check, so a lane that
+// must not store passes `bytes` as its offset instead of branching.
+struct OutBuf {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t end;
+    __device__ __forceinline__ OutBuf(void *base, uint32_t bytes)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, CoherentBuf::kWord3)), end(bytes)
+    {
+    }
+    __device__ __forceinline__ void store(uint32_t off, uint32_t v) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(v, rsrc, (int)off, 0, 0);
+    }
+};
+
 // All threads call after their store_agent()s.  Returns true in exactly one
 // workgroup of the `n` that share `counter`: the last to arrive, which then
 // resets the counter for the next use.

@@ -301,22 +301,29 @@ __device__ void emit_bitmap(int n, SelectSmem<MAXN> &sm, Emit emit)
 
 __device__ __forceinline__ bool bitmap_test(const uint32_t *bits, int i) { return (bits[i >> 5] >> (i & 31)) & 1u; }
 
-// Index-order compaction: calls emit(i, pos) for every slot r of this thread
-// whose bit r of `mask` is set, pos its rank in index order among the set
-// bits of the block.  One ballot per row; a row's selected slots get
-// consecutive positions.
-template <int NT, int KPT, int MAXN, typename Emit>
-__device__ void emit_rows(uint64_t mask, SelectSmem<MAXN> &sm, Emit emit)
+// out[pos] = i for every slot i whose key is >= T, pos its rank in index
+// order, for pos < k.  Keys of slots past the end must be 0xFFFFFFFF: as
+// int32 they are negative, below every threshold (T < 2^31).  No branch per
+// row: a lane that stores nothing, or whose position is >= k, gives the
+// store the buffer's end as offset and the range check drops it.
+template <int NT, int KPT, int MAXN>
+__device__ void emit_at_least(const uint32_t (&key)[KPT], uint32_t T, int32_t *out, uint32_t k,
+                              SelectSmem<MAXN> &sm)
 {
+    const int32_t Ts = (int32_t)T;
+    const uint32_t slot0 = (uint32_t)slot_index<KPT>(0);
     uint32_t cnt = 0;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) cnt += (uint32_t)__popcll(__ballot((mask >> r) & 1ull));
+    for (int r = 0; r < KPT; ++r) cnt += (uint32_t)__popcll(__ballot((int32_t)key[r] >= Ts));
     uint32_t tot;
     uint32_t pos = uniform_u32(waves_excl_scan<NT>(cnt, sm.scratch, &tot));
+    const OutBuf ob(out, k * 4u);
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-        const uint64_t m = __ballot((mask >> r) & 1ull);
-        if ((mask >> r) & 1ull) emit(slot_index<KPT>(r), pos + lanes_below(m));
+        const bool c = (int32_t)key[r] >= Ts;
+        const uint64_t m = __ballot(c);
+        const uint32_t off = (pos + lanes_below(m)) * 4u;
+        ob.store(c ? off : ob.end, slot0 + (uint32_t)(r * 64));
         pos += (uint32_t)__popcll(m);
     }
 }

@@ -291,19 +291,16 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     uint32_t fk[KF];
 #pragma unroll
     for (int r = 0; r < KF; ++r) fk[r] = __float_as_uint(load_agent(&score[min(slot_index<KF>(r), F - 1)]));
+    // slots past F get the key 0xFFFFFFFF, which no selection step takes
 #pragma unroll
-    for (int r = 0; r < KF; ++r) fk[r] = (slot_index<KF>(r) < F) ? (fk[r] & 0x7FFFFFFFu) : 0u;
+    for (int r = 0; r < KF; ++r) fk[r] = (slot_index<KF>(r) < F) ? (fk[r] & 0x7FFFFFFFu) : 0xFFFFFFFFu;
     // scores are sign-free: the window is bits 30..0
     const SelectResult st = block_select_window<kFT, KF>(fk, F, k, 30, 0, sm.sel);
     auto put = [&](int i, uint32_t pos) {
         if (pos < (uint32_t)k) sel[pos] = i;
     };
     if (uniform_u32(st.need_eq) == uniform_u32(st.count_eq)) {  // no tie to break: key >= T
-        const uint32_t T_s = uniform_u32(st.T);
-        uint64_t chosen = 0;
-#pragma unroll
-        for (int r = 0; r < KF; ++r) chosen |= (uint64_t)((slot_index<KF>(r) < F) & (fk[r] >= T_s)) << r;
-        emit_rows<kFT, KF>(chosen, sm.sel, put);
+        emit_at_least<kFT, KF>(fk, uniform_u32(st.T), sel, (uint32_t)k, sm.sel);
     } else {
         selection_bitmap<kFT, KF>(fk, F, st, sm.sel);
         emit_bitmap<kFT>(F, sm.sel, put);
