@@ -191,12 +191,6 @@ def main():
             per[name].append(1000.0 * row[j].elapsed_time(row[j + 1]))
         lat.append(1000.0 * row[0].elapsed_time(row[5]))
     step_us = {n: statistics.mean(v) for n, v in per.items()}
-    # Stage 1 is one kernel for a single token (the first mark pair brackets
-    # it); the marks themselves add a few µs each to what they bracket
-    stage1_us = step_us["xselect"] + step_us["proxy"] + step_us["topk"]
-    kern_us = {"stage1": stage1_us, "gateup": step_us["gateup"], "down": step_us["down"]}
-    kern_bytes = {"stage1": parts["x"] + parts["proxy"] + parts["scales"] + parts["sel"],
-                  "gateup": parts["gateup"] + parts["x"] + 4 * B * k, "down": parts["down"] + parts["out"] + 4 * B * k}
     lat.sort()
     latency = dict(median=lat[len(lat) // 2], p10=lat[len(lat) // 10], p90=lat[(9 * len(lat)) // 10])
 
@@ -232,13 +226,18 @@ def main():
             print("graph capture unavailable: %r" % (exc,), file=sys.stderr)
     print("graph %s us/layer" % graph_us, file=sys.stderr, flush=True)
 
-    # ---- the dominant kernel alone: a graph of back-to-back launches
-    dom = max(kern_us, key=kern_us.get)
-    dom_us, dom_kernel = kern_us[dom], None
-    if dom == "stage1":
-        dom_kernel = "stage1_fused_kernel" if B == 1 else "proxy_kernel"
-        sel_buf = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
-        n_l = 4 * R
+    # ---- each stage alone, live: a HIP graph of back-to-back launches of
+    # that stage (cycling the weight sets) replayed between two events on the
+    # graph's stream.  For one token each stage is one kernel.
+    sels = []
+    for r in range(R):
+        w, p = sets[r]
+        sels.append(P.stage1_select(x, w, p, keep, sp, workspace=ws) if k not in (0, F) else None)
+    torch.cuda.synchronize()
+    sel_buf = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
+    n_l = 4 * R
+
+    def live_us(launch):
         try:
             g1 = torch.cuda.CUDAGraph()
             s1 = torch.cuda.Stream()
@@ -246,8 +245,7 @@ def main():
             with torch.cuda.stream(s1):
                 with torch.cuda.graph(g1, stream=s1):
                     for i in range(n_l):
-                        w, p = sets[i % R]
-                        P.stage1_select(x, w, p, keep, sp, workspace=ws, sel_out=sel_buf)
+                        launch(i)
             torch.cuda.synchronize()
             for _ in range(3):
                 g1.replay()
@@ -258,9 +256,32 @@ def main():
                 g1.replay()
             e1.record()
             torch.cuda.synchronize()
-            dom_us = 1000.0 * e0.elapsed_time(e1) / (n_rep * n_l)
+            return 1000.0 * e0.elapsed_time(e1) / (n_rep * n_l)
         except Exception as exc:  # pragma: no cover
-            print("stage-1 graph timing unavailable (%r); using the marked step time" % (exc,), file=sys.stderr)
+            print("stage graph timing unavailable (%r)" % (exc,), file=sys.stderr)
+            return None
+
+    def s1_launch(i):
+        w, p = sets[i % R]
+        P.stage1_select(x, w, p, keep, sp, workspace=ws, sel_out=sel_buf)
+
+    def s2_launch(i):
+        w, _ = sets[i % R]
+        P.stage2_exact(x, w, sels[i % R], out=out, workspace=ws)
+
+    has_s1 = k not in (0, F)
+    kern_us = {}
+    if has_s1:
+        kern_us["stage1"] = live_us(s1_launch) or (step_us["xselect"] + step_us["proxy"] + step_us["topk"])
+        kern_us["stage2"] = live_us(s2_launch) or (step_us["gateup"] + step_us["down"])
+    else:
+        kern_us["stage2"] = step_us["gateup"] + step_us["down"]
+    kern_bytes = {"stage1": parts["x"] + parts["proxy"] + parts["scales"] + parts["sel"],
+                  "stage2": parts["gateup"] + parts["down"] + parts["x"] + parts["out"] + parts["sel"]}
+    one_kernel = {"stage1": "stage1_fused_kernel" if (B == 1 and d <= 8192 and F <= 16384) else None,
+                  "stage2": "stage2_fused_kernel" if B == 1 else None}
+    dom = max(kern_us, key=kern_us.get)
+    dom_us, dom_kernel = kern_us[dom], one_kernel[dom]
     dom_bytes = kern_bytes[dom]
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
     wl_name = "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s" % (args.workload, d, F, dtype, B, sp, keep, mode)
@@ -341,6 +362,8 @@ def main():
         "latency_us": {kk: round(v, 2) for kk, v in latency.items()},
         "graph_us_per_layer": None if graph_us is None else round(graph_us, 3),
         "kernels_us": {kk: round(v, 3) for kk, v in kern_us.items()},
+        "kernels": {kk: one_kernel[kk] for kk in kern_us},
+        "step_marks_us": {kk: round(v, 3) for kk, v in step_us.items()},
         "kernels_gbps": {kk: round(kern_bytes[kk] / (kern_us[kk] * 1e-6) / 1e9, 1) for kk in kern_us},
         "roofline": roofline,
         "dense_us_per_layer": None if dense_us is None else round(dense_us, 3),

@@ -21,8 +21,8 @@ constexpr int kMaxBatchInt4 = 4;
 // by the last workgroup to use it.
 constexpr int kCounters = kS2SyncBase + kS2SyncWords;
 constexpr int kZeroWords = kCounters;
-// The ticket words and the timeout flag: what a call clears on entry where it
-// does not rely on the previous call having left them zero.
+// The ticket words and the timeout flag: the batched Stage 1 clears them
+// again on entry, inside its first kernel.
 constexpr int kTicketWords = kS2TimeoutSlot + 1;
 constexpr int kTargetProxyBlocks = 1024;
 
@@ -251,7 +251,6 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     const int64_t F = w->d_ff;
     if (k == 0 || k == F) {  // no Stage 1
         TRY_HIP(mark(ev, 0, st));
-        TRY_HIP(launch_zero_u32(ws.counters, kTicketWords, st));
         TRY_HIP(mark(ev, 1, st));
         TRY_HIP(mark(ev, 2, st));
         return run_stage2(x, B, w, nullptr, k, residual, out, k ? sel_out : nullptr, ws, st, ev);
@@ -418,7 +417,6 @@ prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *
     if (x == out) return PROX_ERR_INVALID_ARG;
     const Workspace ws = layout(w->d_model, w->d_ff, batch, PROX_Q_INT8_ROW, workspace);
     if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
-    TRY_HIP(launch_zero_u32(ws.counters, kTicketWords, stream));
     return run_stage2(x, batch, w, sel_idx, k, nullptr, out, nullptr, ws, stream);
 }
 

@@ -28,7 +28,9 @@
  *  - One workspace must not be used by two calls that may run concurrently.
  *    Its first 278528 bytes hold counters that must be zero before the
  *    workspace's first use (prox_workspace_init, or any zero fill); every
- *    call leaves them zero again.  The rest means nothing between calls.
+ *    call leaves them zero again.  After a call that returned PROX_ERR_HIP
+ *    its kernels may have stopped part-way: zero them again before the next
+ *    use.  The rest means nothing between calls.
  *
  * Notation: d = d_model, F = d_ff, B = batch, bf16 = bfloat16 bit patterns.
  */
