@@ -80,6 +80,13 @@ def _bind(lib):
     lib.oracle_proxy.argtypes = [P, I, I, I, ctypes.c_int, P, P, P, P, P, P, P]
     lib.oracle_ffn_masked.argtypes = [P, I, I, I, P, P, P, P, I, P, P]
     lib.oracle_rmsnorm.argtypes = [P, I, I, D, P]
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+    lib.oracle_e4m3_decode.restype = D
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_int
+    lib.oracle_quantize_fp8_row.argtypes = [P, I, I, P, P]
+    lib.oracle_dequant_fp8_f32.argtypes = [P, P, I, I, P]
+    lib.oracle_ffn_masked_fp8.argtypes = [P, I, I, I, P, P, P, P, P, P, P, I, P, P]
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -141,6 +148,58 @@ def quantize(w: np.ndarray, mode: str):
         sc = np.empty((F, d // 128), dtype=np.float32)
         lib.oracle_quantize_int4_g128(_p(w), F, d, _p(q), _p(sc))
     return q, sc
+
+
+def e4m3_decode(c: int) -> float:
+    """Value of one OCP E4M3 code (NaN for S.1111.111)."""
+    return _load().oracle_e4m3_decode(int(c))
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest OCP E4M3 code to a binary32 value (ties to even, saturating at 448)."""
+    return _load().oracle_e4m3_encode(float(np.float32(v)))
+
+
+def quantize_fp8(w: np.ndarray):
+    """FP8 (E4M3) copy of one weight matrix, one binary32 scale per row.
+
+    Returns (codes uint8 [R][C], scales float32 [R])."""
+    w = as_f32(w)
+    R, C = w.shape
+    q = np.empty((R, C), dtype=np.uint8)
+    sc = np.empty((R,), dtype=np.float32)
+    _load().oracle_quantize_fp8_row(_p(w), R, C, _p(q), _p(sc))
+    return q, sc
+
+
+def dequant_fp8_f32(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    """fl32(scale * decode(code)) per element: the binary32 weights an FP8 matrix stands for."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.float32)
+    R, C = q.shape
+    w = np.empty((R, C), dtype=np.float32)
+    _load().oracle_dequant_fp8_f32(_p(q), _p(sc), R, C, _p(w))
+    return w
+
+
+def ffn_masked_fp8(x: np.ndarray, fp8, sel: np.ndarray):
+    """Stage-2 exact SwiGLU on FP8 weights, fp8 = (qg, sg, qu, su, qd, sd) from
+    ``quantize_fp8`` of W_gate, W_up [F][d] and W_down [d][F].
+
+    Returns (y [B][d] binary64, s [B][k])."""
+    x = np.atleast_2d(as_f64(x))
+    B, d = x.shape
+    qg, sg, qu, su, qd, sd = [np.ascontiguousarray(a) for a in fp8]
+    F = qg.shape[0]
+    assert qg.shape == (F, d) and qu.shape == (F, d) and qd.shape == (d, F)
+    assert qg.dtype == np.uint8 and sg.dtype == np.float32 and sd.shape == (d,)
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    k = sel.size
+    y = np.empty((B, d))
+    s = np.empty((B, k))
+    _load().oracle_ffn_masked_fp8(_p(x), B, d, F, _p(qg), _p(sg), _p(qu), _p(su), _p(qd), _p(sd), _p(sel), k,
+                                  _p(s), _p(y))
+    return y, s
 
 
 def topk_ascending(v: np.ndarray, k: int):
@@ -213,23 +272,25 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-5) -> np.ndarray:
 
 # --------------------------------------------------------- whole forward
 
-def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float, mode: str):
+def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float, mode: str, fp8=None):
     """The Prox forward, step by step.
 
     proxy_q = (codes_gate, scales_gate, codes_up, scales_up) from ``quantize``.
     Stage 1: sparse x -> proxy g~, u~ -> salience -> top-k mask (shared by
-    gate, up and down).  Stage 2: exact masked SwiGLU with dense x.
+    gate, up and down).  Stage 2: exact masked SwiGLU with dense x; with
+    ``fp8`` = (qg, sg, qu, su, qd, sd), on those FP8 weights instead of
+    wg, wu, wd (which may then be None).
     Returns a dict with k_in, k, xhat, score, sel, T (k-th score), y, s."""
     x = np.atleast_2d(x)
     B, d = x.shape
-    F = np.asarray(wg).shape[0]
+    F = (np.asarray(wg) if fp8 is None else fp8[0]).shape[0]
     k_in = input_count(input_keep, d)
     k = channel_count(ffn_sparsity, F)
     xhat = input_select(x, k_in)
     qg, scg, qu, scu = proxy_q
     gt, ut, score = proxy(xhat, qg, scg, qu, scu, mode)
     sel, T = topk_ascending(score, k)
-    y, s = ffn_masked(x, wg, wu, wd, sel)
+    y, s = ffn_masked(x, wg, wu, wd, sel) if fp8 is None else ffn_masked_fp8(x, fp8, sel)
     return dict(k_in=k_in, k=k, xhat=xhat, g_proxy=gt, u_proxy=ut, score=score, sel=sel, T=T, y=y, s=s)
 
 

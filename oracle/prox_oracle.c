@@ -276,6 +276,113 @@ void oracle_ffn_masked(const double *x, int64_t B, int64_t d, int64_t F,
 }
 
 /* ------------------------------------------------------------------ */
+/* FP8 exact weights.  The pages claim Prox composes with FP8 model     */
+/* quantization (technical summary, Experimental Results and            */
+/* Significance and Claims) but give no scheme.  Reading: OCP E4M3 --   */
+/* 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 */
+/* holds the subnormals m * 2^-9; no infinities; S.1111.111 is NaN; the */
+/* largest finite magnitude is 448 -- with one binary32 scale per output */
+/* row: scale = fl32(amax / 448); code = the E4M3 value nearest to      */
+/* fl32(w / scale), ties to the even code, magnitudes above 448         */
+/* saturating to 448; the code's sign is the quotient's sign bit.  An   */
+/* all-zero row gets scale 0 and codes 0.                               */
+/* ------------------------------------------------------------------ */
+double oracle_e4m3_decode(int c)
+{
+    int sgn = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* The finite magnitudes 0x00..0x7E increase with the code, so the nearest */
+/* one is found by searching that ordered table.                           */
+int oracle_e4m3_encode(float v)
+{
+    int sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    int lo = 0, hi = 0x7E; /* largest code whose magnitude is <= a */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (oracle_e4m3_decode(mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo; /* decode(c) <= a < decode(c + 1), c + 1 <= 0x7E */
+    double below = a - oracle_e4m3_decode(c), above = oracle_e4m3_decode(c + 1) - a;
+    if (above < below || (above == below && ((c + 1) & 1) == 0)) c = c + 1;
+    return sign | c;
+}
+
+/* w: [rows][cols] binary32; q: [rows][cols] E4M3 codes; scale: [rows] */
+void oracle_quantize_fp8_row(const float *w, int64_t rows, int64_t cols, uint8_t *q, float *scale)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const float *wr = w + r * cols;
+        float a = 0.0f;
+        for (int64_t i = 0; i < cols; ++i)
+            if (fabsf(wr[i]) > a) a = fabsf(wr[i]);
+        float sc = a / 448.0f;
+        scale[r] = sc;
+        for (int64_t i = 0; i < cols; ++i) q[r * cols + i] = (uint8_t)(sc == 0.0f ? 0 : oracle_e4m3_encode(wr[i] / sc));
+    }
+}
+
+/* The binary32 weights an FP8 layer stands for, as its proxy is built     */
+/* from them: w = fl32(scale[r] * decode(q)).                              */
+void oracle_dequant_fp8_f32(const uint8_t *q, const float *scale, int64_t rows, int64_t cols, float *w)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < cols; ++i) w[r * cols + i] = scale[r] * (float)oracle_e4m3_decode(q[r * cols + i]);
+}
+
+/* Stage 2 on FP8 weights: the masked SwiGLU of oracle_ffn_masked with each */
+/* weight taken as scale * decode(code), exact in binary64 (24 + 4          */
+/* significant bits).  qg, qu: [F][d], scales [F]; qd: [d][F] (W_down,      */
+/* nn.Linear orientation), scales [d].                                      */
+void oracle_ffn_masked_fp8(const double *x, int64_t B, int64_t d, int64_t F,
+                           const uint8_t *qg, const float *sg, const uint8_t *qu, const float *su,
+                           const uint8_t *qd, const float *sd, const int64_t *sel, int64_t k,
+                           double *s_out, double *y)
+{
+    double *s = (double *)malloc((size_t)(B * k > 0 ? B * k : 1) * sizeof(double));
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < k; ++r) {
+        int64_t j = sel[r];
+        for (int64_t b = 0; b < B; ++b) {
+            const double *xb = x + b * d;
+            double g = 0.0, u = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                g += (double)sg[j] * oracle_e4m3_decode(qg[j * d + i]) * xb[i];
+                u += (double)su[j] * oracle_e4m3_decode(qu[j * d + i]) * xb[i];
+            }
+            s[b * k + r] = oracle_silu(g) * u;
+        }
+    }
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < d; ++m) {
+        for (int64_t b = 0; b < B; ++b) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < k; ++t)
+                acc += (double)sd[m] * oracle_e4m3_decode(qd[m * F + sel[t]]) * s[b * k + t];
+            y[b * d + m] = acc;
+        }
+    }
+    if (s_out) memcpy(s_out, s, (size_t)(B * k) * sizeof(double));
+    free(s);
+}
+
+/* ------------------------------------------------------------------ */
 /* RMSNorm with unit gain, for a stack of FFN layers (the pages do not  */
 /* describe the layer glue): r = h / sqrt(mean(h^2) + eps).            */
 /* ------------------------------------------------------------------ */

@@ -30,6 +30,14 @@ MUTANTS = [
     ("one input too few kept", "for (int64_t t = 0; t < k_in; ++t)", "for (int64_t t = 0; t + 1 < k_in; ++t)"),
     ("rmsnorm without eps", "sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d)"),
     ("silu missing z", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("e4m3 exponent bias 8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3 subnormals 2^-10", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("e4m3 ties away from zero", "(above == below && ((c + 1) & 1) == 0)", "(above == below)"),
+    ("e4m3 no saturation", "if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
+    ("fp8 scale for max 240", "float sc = a / 448.0f;", "float sc = a / 240.0f;"),
+    ("fp8 up uses gate scale", "u += (double)su[j] *", "u += (double)sg[j] *"),
+    ("fp8 down scale per column", "acc += (double)sd[m] * oracle_e4m3_decode(qd[m * F + sel[t]])",
+     "acc += (double)sd[sel[t] % d] * oracle_e4m3_decode(qd[m * F + sel[t]])"),
 ]
 
 

@@ -358,6 +358,126 @@ def test_zero_sparsity_is_dense_and_stage2_uses_dense_x(oracle):
     assert r1["k"] == 0 and not r1["y"].any()
 
 
+# ------------------------------------------------------------- FP8 E4M3
+# Facts of the OCP E4M3 format (not of the pages, which name FP8 only):
+# bias 7, subnormals down to 2^-9, largest finite 448, S.1111.111 = NaN.
+
+def _e4m3_values(oracle):
+    return np.array([oracle.e4m3_decode(c) for c in range(256)])
+
+
+def test_e4m3_decode_spec_values(oracle):
+    # catches a wrong exponent bias, subnormal scale or NaN encoding
+    spec = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3F: 1.875,
+            0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in spec.items():
+        assert oracle.e4m3_decode(c) == v, hex(c)
+    assert math.isnan(oracle.e4m3_decode(0x7F)) and math.isnan(oracle.e4m3_decode(0xFF))
+    assert math.copysign(1.0, oracle.e4m3_decode(0x80)) == -1.0 and oracle.e4m3_decode(0x80) == 0.0
+
+
+def test_e4m3_decode_structure(oracle):
+    # magnitudes rise with the code; the sign bit negates; each binade holds
+    # 8 evenly spaced values; the subnormals continue the first binade's step
+    v = _e4m3_values(oracle)
+    mag = v[:0x7F]
+    assert np.all(np.diff(mag) > 0)
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+    for e in range(1, 16):
+        row = v[8 * e:8 * e + 8] if e < 15 else v[8 * e:8 * e + 7]
+        steps = np.diff(np.concatenate([row, [2.0 ** (e - 6)]])) if e < 15 else np.diff(row)
+        assert np.all(steps == steps[0]) and steps[0] == 2.0 ** (e - 10), e
+    assert np.all(np.diff(v[0:9]) == 2.0 ** -9)
+    assert np.isfinite(v).sum() == 254
+
+
+def _nearest_code_brute(v, table):
+    # the definition of the conversion by exhaustive search: nearest finite
+    # value, ties to the code with an even mantissa, saturation at 448
+    a = abs(float(v))
+    sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+    if a >= 448.0:
+        return sign | 0x7E
+    dist = np.abs(table[:0x7F] - a)
+    best = np.flatnonzero(dist == dist.min())
+    if len(best) > 1:
+        best = [c for c in best if c % 2 == 0]
+    return sign | int(best[0])
+
+
+def test_e4m3_encode_nearest_ties_even(oracle):
+    # catches ties away from zero, truncation, missing saturation
+    table = _e4m3_values(oracle)
+    rng = np.random.default_rng(11)
+    vals = list(np.float32(rng.uniform(-1, 1, 400) * 2.0 ** rng.uniform(-12, 9.5, 400)))
+    mags = table[:0x7F]
+    vals += list(np.float32((mags[1:] + mags[:-1]) / 2))          # every midpoint (a tie)
+    vals += list(np.float32(-(mags[1:] + mags[:-1]) / 2))
+    vals += list(np.float32(mags)) + [np.float32(449.0), np.float32(464.0), np.float32(1e30), np.float32(-600.0)]
+    for v in vals:
+        assert oracle.e4m3_encode(v) == _nearest_code_brute(v, table), float(v)
+    assert oracle.e4m3_encode(np.float32(-0.0)) == 0x80 and oracle.e4m3_encode(np.float32(0.0)) == 0x00
+    for c in range(256):
+        if c not in (0x7F, 0xFF):
+            assert oracle.e4m3_encode(np.float32(table[c])) == c, hex(c)
+
+
+def test_quantize_fp8_rows(oracle):
+    # the absmax element reaches +-448; every code is finite; error at most
+    # half a step of E4M3 at the scaled magnitude; an all-zero row stays zero
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((6, 300)) * np.array([[1e-3], [0.02], [1.0], [50.0], [0.0], [3e-6]])).astype(np.float32)
+    w[5, 17] = -0.25
+    q, sc = oracle.quantize_fp8(w)
+    table = _e4m3_values(oracle)
+    assert sc[4] == 0.0 and not q[4].any()
+    for r in range(6):
+        if r == 4:
+            continue
+        a = np.abs(w[r]).max()
+        i = int(np.abs(w[r]).argmax())
+        assert q[r, i] & 0x7F == 0x7E and (q[r, i] >> 7) == (w[r, i] < 0)
+        assert np.float32(a / 448.0) == sc[r] or abs(float(sc[r]) * 448.0 / float(a) - 1.0) < 2 ** -23
+        assert np.all((q[r] & 0x7F) != 0x7F)
+        t = np.abs(w[r].astype(np.float64) / float(sc[r]))
+        err = np.abs(table[q[r]] * float(sc[r]) - w[r].astype(np.float64)) / float(sc[r])
+        step = np.where(t >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 3), 2.0 ** -9)
+        assert np.all(err <= step / 2 * (1 + 1e-6) + 1e-30)
+
+
+def test_ffn_masked_fp8_equals_masked_on_exact_weights(oracle):
+    # rows whose absmax is 1.75 * 2^e get the scale 2^(e-8) exactly, so
+    # scale * decode is exact in binary32: the FP8 Stage 2 must then equal the
+    # pinned masked FFN on those dequantized weights, bit for bit.  The
+    # scales differ from row to row, so a scale taken from the wrong row or
+    # projection shows.
+    d, F = 96, 80
+    rng = np.random.default_rng(13)
+
+    def rows(n, m):
+        e = rng.integers(-1, 3, n)
+        w = (rng.uniform(-1.7, 1.7, (n, m)) * 2.0 ** e[:, None]).astype(np.float32)
+        w[np.arange(n), rng.integers(0, m, n)] = (1.75 * 2.0 ** e * np.where(rng.random(n) < 0.5, -1, 1)).astype(np.float32)
+        return w, (2.0 ** (e - 8)).astype(np.float32)
+
+    (wg, eg), (wu, eu), (wd, ed) = rows(F, d), rows(F, d), rows(d, F)
+    qg, sg = oracle.quantize_fp8(wg)
+    qu, su = oracle.quantize_fp8(wu)
+    qd, sd = oracle.quantize_fp8(wd)
+    np.testing.assert_array_equal(sg, eg)
+    np.testing.assert_array_equal(su, eu)
+    np.testing.assert_array_equal(sd, ed)
+    dq = lambda q, s: oracle.dequant_fp8_f32(q, s)
+    x = synth.make_x(2, d, "f32", seed=13)
+    sel = np.sort(rng.choice(F, size=29, replace=False))
+    y8, s8 = oracle.ffn_masked_fp8(x, (qg, sg, qu, su, qd, sd), sel)
+    y, s = oracle.ffn_masked(x, dq(qg, sg), dq(qu, su), dq(qd, sd), sel)
+    np.testing.assert_array_equal(s8, s)
+    np.testing.assert_array_equal(y8, y)
+    # and the dequantized weights are the table values times the row's power of two
+    np.testing.assert_array_equal(dq(qg, sg), (_e4m3_values(oracle)[qg] * eg[:, None].astype(np.float64)).astype(np.float32))
+
+
 # --------------------------------------------------------------- RMSNorm
 
 def test_rmsnorm_closed_forms(oracle):
