@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--sparsity", type=float, default=None)
     ap.add_argument("--keep", type=float, default=None)
     ap.add_argument("--mode", default=None)
+    ap.add_argument("--wformat", default="native", choices=["native", "fp8"],
+                    help="exact (Stage-2) weights in the activation dtype, or FP8 E4M3 with per-row scales")
     ap.add_argument("--sets", type=int, default=4, help="weight copies cycled to defeat the Infinity Cache")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -69,19 +71,20 @@ def kept_union(x_f32: np.ndarray, k_in: int) -> int:
     return int(keep.sum())
 
 
-def algorithmic_bytes(d, F, B, k, k_union, bw, mode):
+def algorithmic_bytes(d, F, B, k, k_union, bw, mode, fp8=False):
     """Bytes the method must move for one layer: x, proxy codes of the kept
     columns (the union over tokens), proxy scales, the selected gate/up/down
-    rows, the mask, the output.  Workspace traffic (partials, scores) is not
-    counted."""
+    rows (one byte per weight with FP8 weights, plus their scales), the mask,
+    the output.  Workspace traffic (partials, scores) is not counted."""
     if mode == "int8_row":
         proxy = 2 * k_union * F
         scales = 2 * F * 4
     else:
         proxy = k_union * F  # two nibbles per byte, gate and up
         scales = (d // 128) * 2 * F * 4
-    return dict(x=B * d * bw, proxy=proxy, scales=scales, gateup=2 * k * d * bw, down=k * d * bw,
-                sel=k * 4, out=B * d * bw)
+    ww = 1 if fp8 else bw
+    return dict(x=B * d * bw, proxy=proxy, scales=scales, gateup=2 * k * d * ww + (8 * k if fp8 else 0),
+                down=k * d * ww + (4 * d if fp8 and k else 0), sel=k * 4, out=B * d * bw)
 
 
 def source_digest() -> str:
@@ -140,11 +143,16 @@ def main():
 
     wg, wu, wd = synth.make_weights(d, F, wl.std, dtype, seed=0, layer=0)
     x_host = synth.make_x(B, d, dtype, seed=0)
-    w0 = P.pack_weights(to_dev(wg), to_dev(wu), to_dev(wd))
+    fp8 = args.wformat == "fp8"
+    w0 = (P.pack_weights_fp8 if fp8 else P.pack_weights)(to_dev(wg), to_dev(wu), to_dev(wd))
     p0 = P.quantize_proxy(w0, mode)
     sets = [(w0, p0)]
     for _ in range(1, args.sets):
-        w = P.Weights(w0.w_gu.clone(), w0.w_down_t.clone(), d, F)
+        if fp8:
+            w = P.Weights(w0.w_gu.clone(), w0.w_down_t.clone(), d, F, act_dtype=w0.act_dtype,
+                          gu_scales=w0.gu_scales.clone(), down_scales=w0.down_scales.clone())
+        else:
+            w = P.Weights(w0.w_gu.clone(), w0.w_down_t.clone(), d, F)
         p = P.Proxy(p0.codes.clone(), p0.scales.clone(), p0.mode, d, F)
         sets.append((w, p))
     x = to_dev(x_host)
@@ -155,7 +163,7 @@ def main():
 
     k_in, k = P.counts(d, F, keep, sp)
     k_union = kept_union(synth.to_f32(x_host), k_in)
-    parts = algorithmic_bytes(d, F, B, k, k_union, bw, mode)
+    parts = algorithmic_bytes(d, F, B, k, k_union, bw, mode, fp8)
     layer_bytes = sum(parts.values())
     R = len(sets)
 
@@ -284,7 +292,8 @@ def main():
     dom_us, dom_kernel = kern_us[dom], one_kernel[dom]
     dom_bytes = kern_bytes[dom]
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
-    wl_name = "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s" % (args.workload, d, F, dtype, B, sp, keep, mode)
+    wl_name = "%s_ffn_%dx%d_%s_B%d_sp%g_keep%g_%s%s" % (args.workload, d, F, dtype, B, sp, keep, mode,
+                                                         "_fp8w" if fp8 else "")
     traffic = traffic_from_profiles(dom_kernel or dom, wl_name)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom_kernel or dom,
@@ -315,12 +324,18 @@ def main():
     if not args.no_cpu:
         import oracle
         oracle.build(force=False)
-        proxy_q = oracle.quantize(wg, mode) + oracle.quantize(wu, mode)
+        if fp8:  # the oracle's FP8 copy; the proxy is built from its binary32 values
+            f8 = oracle.quantize_fp8(wg) + oracle.quantize_fp8(wu) + oracle.quantize_fp8(wd)
+            proxy_q = (oracle.quantize(oracle.dequant_fp8_f32(f8[0], f8[1]), mode) +
+                       oracle.quantize(oracle.dequant_fp8_f32(f8[2], f8[3]), mode))
+        else:
+            f8 = None
+            proxy_q = oracle.quantize(wg, mode) + oracle.quantize(wu, mode)
         times = []
         deadline = time.time() + 12.0
         while True:
             t = time.perf_counter()
-            ref = oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode)
+            ref = oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode, fp8=f8)
             times.append(time.perf_counter() - t)
             if time.time() > deadline or len(times) >= 40:
                 break
@@ -334,7 +349,8 @@ def main():
         torch.cuda.synchronize()
         sel_np = sel[:k].cpu().numpy().astype(np.int64)
         ok, msg = oracle.mask_admissible(sel_np, ref["sel"], ref["score"], ref["T"], k)
-        y_ref, _ = oracle.ffn_masked(x_host, wg, wu, wd, sel_np)
+        y_ref, _ = (oracle.ffn_masked(x_host, wg, wu, wd, sel_np) if f8 is None else
+                    oracle.ffn_masked_fp8(x_host, f8, sel_np))
         yg = (y.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else y.cpu().numpy())
         yg = oracle.as_f64(yg)
         err = max(float(np.abs(yg[b] - y_ref[b]).max() / np.abs(y_ref[b]).max()) for b in range(B))
@@ -351,10 +367,11 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": dtype + ("+fp8e4m3w" if fp8 else ""),
         "data": "synthetic",
         "config": {"workload": wl_name,
                    "d_model": d, "d_ff": F, "batch": B, "ffn_sparsity": sp, "input_keep": keep, "proxy": mode,
+                   "exact_weights": "fp8_e4m3_row_scaled" if fp8 else dtype,
                    "k": k, "k_in": k_in, "kept_union": k_union, "weight_sets": R},
         "layer_bytes": layer_bytes,
         "layer_gbps": round(layer_gbps, 1),

@@ -5,6 +5,6 @@ this package is its thin Python binding.
 """
 from .prox import (  # noqa: F401
     BF16, F32, MODES, STEP_NAMES, ProxError, Proxy, Weights, alloc_workspace, chain_forward, chain_workspace_size, counts,
-    ffn_forward, ffn_forward_timed, load_library, pack_weights, proxy_sizes, quantize_proxy, rmsnorm, stage1_select, stage2_exact,
-    topk, version, workspace_init, workspace_size,
+    ffn_forward, ffn_forward_timed, load_library, pack_weights, pack_weights_fp8, proxy_sizes, quantize_proxy, rmsnorm,
+    stage1_select, stage2_exact, topk, version, workspace_init, workspace_size, W_FP8_E4M3, W_NATIVE,
 )

@@ -56,7 +56,19 @@ prox_status check_weights(const prox_weights *w)
     prox_status s = check_shape(w->d_model, w->d_ff);
     if (s != PROX_OK) return s;
     if (bad_ptr(w->w_gu) || bad_ptr(w->w_down_t)) return PROX_ERR_INVALID_ARG;
+    if (w->wformat == PROX_W_FP8_E4M3) {
+        if (w->d_model % 16 != 0) return PROX_ERR_UNSUPPORTED;
+        if (bad_ptr(w->gu_scales) || bad_ptr(w->down_scales)) return PROX_ERR_INVALID_ARG;
+    } else if (w->wformat != PROX_W_NATIVE) {
+        return PROX_ERR_UNSUPPORTED;
+    }
     return PROX_OK;
+}
+
+S2Weights s2_weights(const prox_weights *w)
+{
+    const bool fp8 = w->wformat == PROX_W_FP8_E4M3;
+    return S2Weights{fp8 ? 1 : 0, w->w_gu, fp8 ? w->gu_scales : nullptr, w->w_down_t, fp8 ? w->down_scales : nullptr};
 }
 
 prox_status check_proxy(const prox_proxy *p, const prox_weights *w)
@@ -117,10 +129,10 @@ ProxyPlan proxy_plan(int64_t d, int64_t F, int64_t B, int mode)
     return p;
 }
 
-DownPlan down_plan(int64_t d, int64_t k, int64_t B, prox_dtype t)
+DownPlan down_plan(int64_t d, int64_t k, int64_t B, const prox_weights *w)
 {
     DownPlan p;
-    p.vec = 16 / elem_bytes(t);
+    p.vec = w->wformat == PROX_W_FP8_E4M3 ? 8 : 16 / elem_bytes(w->dtype);  // FP8: 8-byte loads
     p.cols = 64 * p.vec;
     p.n_slices = ceil_div(d, p.cols);
     p.S = ceil_div(k > 0 ? k : 1, kDownRowsPerWave * kDownWaves);
@@ -217,16 +229,16 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         return hip_status(mark(ev, 5, st));
     }
     if (B == 1) {  // one launch: the down projection starts while gate/up drains
-        TRY_HIP(launch_stage2_fused(dt, x, (int)d, (int)w->d_ff, w->w_gu, w->w_down_t, sel, (int)k, ws.s_sp,
-                                    ws.down_part, residual, out, ws.counters, iota_out, st));
+        TRY_HIP(launch_stage2_fused(dt, s2_weights(w), x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part,
+                                    residual, out, ws.counters, iota_out, st));
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
-    TRY_HIP(launch_gateup(dt, x, (int)B, (int)d, (int)w->d_ff, w->w_gu, sel, (int)k, ws.s_sp, iota_out, st));
+    TRY_HIP(launch_gateup(dt, s2_weights(w), x, (int)B, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, iota_out, st));
     TRY_HIP(mark(ev, 4, st));
-    const DownPlan dp = down_plan(d, k, B, w->dtype);
-    TRY_HIP(launch_down(dt, dp, ws.s_sp, (int)B, (int)k, w->w_down_t, sel, (int)d, (int)w->d_ff, ws.down_part, residual, out,
-                        ws.counters + kDownSliceBase, st));
+    const DownPlan dp = down_plan(d, k, B, w);
+    TRY_HIP(launch_down(dt, s2_weights(w), dp, ws.s_sp, (int)B, (int)k, sel, (int)d, (int)w->d_ff, ws.down_part,
+                        residual, out, ws.counters + kDownSliceBase, st));
     return hip_status(mark(ev, 5, st));
 }
 
@@ -299,6 +311,22 @@ prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *
                                   w_down_t_out, stream));
 }
 
+prox_status prox_pack_weights_fp8(const void *w_gate, const void *w_up, const void *w_down, int64_t d, int64_t F,
+                                  prox_dtype dtype, void *w_gu_out, float *gu_scales_out, void *w_down_t_out,
+                                  float *down_scales_out, hipStream_t stream)
+{
+    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    prox_status s = check_shape(d, F);
+    if (s != PROX_OK) return s;
+    if (d % 16 != 0) return PROX_ERR_UNSUPPORTED;
+    if (bad_ptr(w_gate) || bad_ptr(w_up) || bad_ptr(w_down) || bad_ptr(w_gu_out) || bad_ptr(gu_scales_out) ||
+        bad_ptr(w_down_t_out) || bad_ptr(down_scales_out))
+        return PROX_ERR_INVALID_ARG;
+    return hip_status(launch_pack_fp8(dtype == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F,
+                                      (uint8_t *)w_gu_out, gu_scales_out, (uint8_t *)w_down_t_out, down_scales_out,
+                                      stream));
+}
+
 prox_status prox_proxy_sizes(int64_t d, int64_t F, prox_qmode mode, size_t *codes_bytes, size_t *scales_bytes)
 {
     if (!codes_bytes || !scales_bytes) return PROX_ERR_INVALID_ARG;
@@ -322,8 +350,9 @@ prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *co
     s = check_mode_shape(w->d_model, w->d_ff, mode);
     if (s != PROX_OK) return s;
     if (bad_ptr(codes) || bad_ptr(scales)) return PROX_ERR_INVALID_ARG;
-    return hip_status(launch_quantize(w->dtype == PROX_F32 ? 0 : 1, mode == PROX_Q_INT4_G128 ? 4 : 8, w->w_gu,
-                                      (int)w->d_model, (int)w->d_ff, (uint8_t *)codes, (float *)scales, stream));
+    return hip_status(launch_quantize(w->dtype == PROX_F32 ? 0 : 1, w->wformat == PROX_W_FP8_E4M3 ? 1 : 0, w->w_gu,
+                                      w->gu_scales, mode == PROX_Q_INT4_G128 ? 4 : 8, (int)w->d_model, (int)w->d_ff,
+                                      (uint8_t *)codes, (float *)scales, stream));
 }
 
 prox_status prox_workspace_size(int64_t d, int64_t F, int64_t B, prox_qmode mode, size_t *bytes)

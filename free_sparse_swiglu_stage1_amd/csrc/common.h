@@ -55,10 +55,49 @@ template <> struct vec16<float> {
     }
 };
 
+// OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities, largest finite 448).  Encoding: the nearest E4M3 value, ties to
+// the even code, magnitudes >= 448 saturating to 448, the sign bit copied
+// (so -0 -> 0x80).  Finite inputs only.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f)  // below 2^-6: subnormal steps of 2^-9 (8 -> the least normal, 0x08)
+        return sign | (uint32_t)rintf(a * 512.0f);
+    // normal: keep 3 mantissa bits of the binary32 value, rounding half to even
+    // at bit 20; a carry moves into the exponent field, as it should
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);  // exponent bias 127 -> 7
+    return sign | min(code, 0x7Eu);
+}
+
+// Four E4M3 codes (byte 0 first) to binary32, by the hardware conversion
+// (gfx950 decodes the OCP format).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *f)
+{
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo[0];
+    f[1] = lo[1];
+    f[2] = hi[0];
+    f[3] = hi[1];
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+
 // streaming 16-byte load of data read exactly once (weights, proxy codes)
 __device__ __forceinline__ u32x4 ld_stream(const void *p)
 {
     return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
+// the same for 8 bytes
+__device__ __forceinline__ u32x2 ld_stream8(const void *p)
+{
+    return __builtin_nontemporal_load((const u32x2 *)p);
 }
 
 // ------------------------------------------------- cross-workgroup data

@@ -60,11 +60,23 @@ hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int 
                         const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st);
 hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st);
 
+// Stage-2 weights as the kernels read them.  fmt 0: w_gu [F][2][d] and
+// w_down_t [F][d] in the activation dtype.  fmt 1: the same layouts in FP8
+// E4M3 codes, with fp32 scales per output row: gu_scales [F][2] (gate, up of
+// channel j), down_scales [d] (row m of W_down).
+struct S2Weights {
+    int fmt;
+    const void *w_gu;
+    const float *gu_scales;
+    const void *w_down_t;
+    const float *down_scales;
+};
+
 // Stage 2 clamps every mask entry into [0, F): a malformed mask gives wrong
 // values, never an access outside the weights.
-hipError_t launch_gateup(int dtype, const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel,
+hipError_t launch_gateup(int dtype, const S2Weights &w, const void *x, int B, int d, int F, const int32_t *sel,
                          int k, float *s_sp, int32_t *iota_out, hipStream_t st);
-hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
+hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const float *s_sp, int B, int k,
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
 // Stage 2 for one token in one launch (stage2.hip).  Counter slots:
@@ -86,16 +98,19 @@ __host__ __device__ constexpr int s2_sync_line(int s)
 {
     return kS2SyncBase + (s % kS2SyncPages) * kS2PageWords + (s / kS2SyncPages) * kS2LineWords;
 }
-hipError_t launch_stage2_fused(int dtype, const void *x, int d, int F, const void *w_gu, const void *w_down_t,
-                               const int32_t *sel, int k, float *s_sp, float *part, const void *residual, void *out,
-                               uint32_t *counters, int32_t *iota_out, hipStream_t st);
+hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int d, int F, const int32_t *sel, int k,
+                               float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
+                               int32_t *iota_out, hipStream_t st);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
 
 hipError_t launch_pack(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,
                        void *w_gu, void *w_down_t, hipStream_t st);
-hipError_t launch_quantize(int dtype, int qbits, const void *w_gu, int d, int F, uint8_t *codes, float *scales,
-                           hipStream_t st);
+hipError_t launch_pack_fp8(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,
+                           uint8_t *w_gu8, float *gu_scales, uint8_t *w_down_t8, float *down_scales, hipStream_t st);
+// proxy quantization from w_gu in the activation dtype (wfmt 0) or FP8 (wfmt 1, with gu_scales)
+hipError_t launch_quantize(int dtype, int wfmt, const void *w_gu, const float *gu_scales, int qbits, int d, int F,
+                           uint8_t *codes, float *scales, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, const void *h, int B, int d, float eps, void *out, hipStream_t st);
 
 }  // namespace prox

@@ -32,10 +32,26 @@ __device__ __forceinline__ void load_rows_regs(const T *__restrict__ x, int B, i
     }
 }
 
-template <typename T, int NB>
+// x in LDS, optionally padded: with CH > 0, 4 floats of padding follow every
+// CH elements, so that lanes reading consecutive CH-element chunks with
+// 16-byte reads hit distinct banks (a chunk of 16 floats read per lane is a
+// 64-byte stride: 4-way conflicts without the padding, none with it).
+template <int CH>
+__host__ __device__ constexpr int xpad_index(int i)
+{
+    return CH > 0 ? i + (i / CH) * 4 : i;
+}
+template <int CH>
+__host__ __device__ constexpr int xpad_row(int d)
+{
+    return xpad_index<CH>(d);
+}
+
+template <typename T, int NB, int CH>
 __device__ __forceinline__ void store_rows_lds(const u32x4 (&xr)[kStageRegs], int B, int d, float *xs)
 {
     constexpr int V = vec16<T>::N;
+    static_assert(CH == 0 || CH % V == 0, "an x vector must not straddle padding");
     const int nvec = NB * d / V;
 #pragma unroll
     for (int q = 0; q < kStageRegs; ++q) {
@@ -43,9 +59,11 @@ __device__ __forceinline__ void store_rows_lds(const u32x4 (&xr)[kStageRegs], in
         if (e < nvec) {
             float f[V];
             vec16<T>::unpack(xr[q], f);
-            const bool live = (e * V) / d < B;
+            const int b = (e * V) / d;
+            const bool live = b < B;
+            float *dst = xs + b * xpad_row<CH>(d) + xpad_index<CH>(e * V - b * d);
 #pragma unroll
-            for (int i = 0; i < V; ++i) xs[e * V + i] = live ? f[i] : 0.0f;
+            for (int i = 0; i < V; ++i) dst[i] = live ? f[i] : 0.0f;
         }
     }
     __syncthreads();
@@ -53,10 +71,11 @@ __device__ __forceinline__ void store_rows_lds(const u32x4 (&xr)[kStageRegs], in
 
 // Stage rows [0, min(B, NB)) of a [B][d] tensor into LDS as fp32 (rows up to
 // NB zero-filled), 16-byte loads, all of a thread's loads issued before use.
-template <typename T, int NB>
+template <typename T, int NB, int CH>
 __device__ __forceinline__ void stage_rows_f32(const T *__restrict__ x, int B, int d, float *xs)
 {
     constexpr int V = vec16<T>::N;
+    static_assert(CH == 0 || CH % V == 0, "an x vector must not straddle padding");
     constexpr int PER = 2;  // 16-byte loads per thread per batch
     const int nvec = NB * d / V;
     for (int e0 = threadIdx.x; e0 < nvec; e0 += 256 * PER) {
@@ -74,38 +93,94 @@ __device__ __forceinline__ void stage_rows_f32(const T *__restrict__ x, int B, i
             if (e < nvec) {
                 float f[V];
                 vec16<T>::unpack(v[q], f);
-                const bool live = (e * V) / d < B;
+                const int b = (e * V) / d;
+                const bool live = b < B;
+                float *dst = xs + b * xpad_row<CH>(d) + xpad_index<CH>(e * V - b * d);
 #pragma unroll
-                for (int i = 0; i < V; ++i) xs[e * V + i] = live ? f[i] : 0.0f;
+                for (int i = 0; i < V; ++i) dst[i] = live ? f[i] : 0.0f;
             }
         }
     }
     __syncthreads();
 }
 
+// How Stage 2 streams weight rows of element type TW (float, bf16 bits, or
+// FP8 E4M3 codes as uint8_t): gate/up rows in 16-byte vectors of GV
+// elements, UNR per lane per row and pass; down rows in DV elements per
+// lane (16 bytes, or 8 for FP8 so that a slice stays 512 columns wide).
+template <typename TW> struct WRows;
+template <> struct WRows<float> {
+    static constexpr int GV = 4, UNR = 8, DV = 4;
+    using dvec = u32x4;
+    static __device__ __forceinline__ void gunpack(const u32x4 &v, float *f) { vec16<float>::unpack(v, f); }
+    static __device__ __forceinline__ dvec dload(const float *p) { return ld_stream(p); }
+    static __device__ __forceinline__ void dunpack(const dvec &v, float *f) { vec16<float>::unpack(v, f); }
+};
+template <> struct WRows<uint16_t> {
+    static constexpr int GV = 8, UNR = 8, DV = 8;
+    using dvec = u32x4;
+    static __device__ __forceinline__ void gunpack(const u32x4 &v, float *f) { vec16<uint16_t>::unpack(v, f); }
+    static __device__ __forceinline__ dvec dload(const uint16_t *p) { return ld_stream(p); }
+    static __device__ __forceinline__ void dunpack(const dvec &v, float *f) { vec16<uint16_t>::unpack(v, f); }
+};
+template <> struct WRows<uint8_t> {
+    static constexpr int GV = 16, UNR = 4, DV = 8;
+    using dvec = u32x2;
+    static __device__ __forceinline__ void gunpack(const u32x4 &v, float *f)
+    {
+        e4m3x4_to_f32(v.x, f);
+        e4m3x4_to_f32(v.y, f + 4);
+        e4m3x4_to_f32(v.z, f + 8);
+        e4m3x4_to_f32(v.w, f + 12);
+    }
+    static __device__ __forceinline__ dvec dload(const uint8_t *p) { return ld_stream8(p); }
+    static __device__ __forceinline__ void dunpack(const dvec &v, float *f)
+    {
+        e4m3x4_to_f32(v.x, f);
+        e4m3x4_to_f32(v.y, f + 4);
+    }
+};
+
+// x padding chunk of gateup_block: a lane reads GV consecutive x values per
+// weight vector; pad when that stride would conflict (GV >= 8), for one
+// token only (4 tokens of padded x would not fit the 64 KB the batched
+// launch allows).
+template <typename TW, int NB>
+__host__ __device__ constexpr int gu_xpad()
+{
+    return (NB == 1 && WRows<TW>::GV >= 8) ? WRows<TW>::GV : 0;
+}
+
 // One gate/up workgroup (4 waves, one selected channel each: ranks
 // 4 blk .. 4 blk + 3).  xs: LDS for x as fp32, [NB][d].  COHERENT: s is stored with
-// device-coherent stores, for other workgroups of the same launch.
-template <typename T, int NB, bool COHERENT>
+// device-coherent stores, for other workgroups of the same launch.  gsc: the
+// FP8 scales [F][2], applied to the finished dot products (else null).
+template <typename T, typename TW, int NB, bool COHERENT>
 __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int d, int F,
-                                             const T *__restrict__ w_gu, const int32_t *__restrict__ sel, int k,
-                                             float *__restrict__ s_sp, int32_t *__restrict__ iota_out, float *xs,
-                                             int blk)
+                                             const TW *__restrict__ w_gu, const float *__restrict__ gsc,
+                                             const int32_t *__restrict__ sel, int k, float *__restrict__ s_sp,
+                                             int32_t *__restrict__ iota_out, float *xs, int blk)
 {
-    constexpr int V = vec16<T>::N;  // elements per 16-byte load
-    constexpr int UNR = 8;          // 16-byte vectors per lane per pass (two rows: 2*UNR loads)
+    constexpr int V = WRows<TW>::GV;     // elements per 16-byte load
+    constexpr int UNR = WRows<TW>::UNR;  // 16-byte vectors per lane per pass (two rows: 2*UNR loads)
+    constexpr int CH = gu_xpad<TW, NB>();  // x padding chunk in LDS (0: none)
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     (void)tid;
     const int r = blk * 4 + wv;  // one selected channel per wave
     const bool live = r < k;
     const int j = (int)min((uint32_t)(live ? (sel ? sel[r] : r) : (sel ? sel[0] : 0)), (uint32_t)(F - 1));
     if (iota_out && live && lane == 0) iota_out[r] = r;
-    const T *grow = w_gu + (int64_t)j * 2 * d;
-    const T *urow = grow + d;
+    const TW *grow = w_gu + (int64_t)j * 2 * d;
+    const TW *urow = grow + d;
     const int nv = d / V;  // 16-byte vectors per row
+    float gs = 1.0f, us = 1.0f;
+    if (gsc) {
+        gs = gsc[2 * j];
+        us = gsc[2 * j + 1];
+    }
 
     // x first (vmcnt retires in order: waiting for x must not wait for the rows)
-    const bool x_in_regs = NB * nv <= 256 * kStageRegs;
+    const bool x_in_regs = NB * (d / vec16<T>::N) <= 256 * kStageRegs;  // x's own 16-byte vectors
     u32x4 xr[kStageRegs];
     if (x_in_regs) load_rows_regs<T, NB>(x, B, d, xr);
     // first pass of both rows, every load issued (clamped index), no branches
@@ -117,9 +192,9 @@ __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int
         vu[u] = ld_stream(urow + vi * V);
     }
     if (x_in_regs)
-        store_rows_lds<T, NB>(xr, B, d, xs);
+        store_rows_lds<T, NB, CH>(xr, B, d, xs);
     else
-        stage_rows_f32<T, NB>(x, B, d, xs);
+        stage_rows_f32<T, NB, CH>(x, B, d, xs);
 
     float ag[NB], au[NB];
 #pragma unroll
@@ -138,11 +213,11 @@ __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int
             const int vi = base + lane + u * 64;
             if (vi < nv) {
                 float fg[V], fu[V];
-                vec16<T>::unpack(vg[u], fg);
-                vec16<T>::unpack(vu[u], fu);
+                WRows<TW>::gunpack(vg[u], fg);
+                WRows<TW>::gunpack(vu[u], fu);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    const float *xb = xs + b * d + vi * V;
+                    const float *xb = xs + b * xpad_row<CH>(d) + xpad_index<CH>(vi * V);
 #pragma unroll
                     for (int q = 0; q < V; ++q) {
                         ag[b] = fmaf(fg[q], xb[q], ag[b]);
@@ -154,8 +229,8 @@ __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const float g = wave_sum(ag[b]);
-        const float u = wave_sum(au[b]);
+        const float g = gs * wave_sum(ag[b]);
+        const float u = us * wave_sum(au[b]);
         if (live && lane == 0 && b < B) {
             if (COHERENT)
                 store_agent(&s_sp[(int64_t)b * k + r], silu(g) * u);
@@ -165,13 +240,14 @@ __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int
     }
 }
 
-template <typename T, int NB>
+template <typename T, typename TW, int NB>
 __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d, int F,
-                                                     const T *__restrict__ w_gu, const int32_t *__restrict__ sel,
-                                                     int k, float *__restrict__ s_sp, int32_t *__restrict__ iota_out)
+                                                     const TW *__restrict__ w_gu, const float *__restrict__ gsc,
+                                                     const int32_t *__restrict__ sel, int k, float *__restrict__ s_sp,
+                                                     int32_t *__restrict__ iota_out)
 {
     extern __shared__ float xs[];  // [NB][d]
-    gateup_block<T, NB, false>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, xs, blockIdx.x);
+    gateup_block<T, TW, NB, false>(x, B, d, F, w_gu, gsc, sel, k, s_sp, iota_out, xs, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------
@@ -191,15 +267,15 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
 // in LDS in wave order into this split's partial (coherent 64-bit stores);
 // the last split of the slice to finish (ticket) adds the partials --
 // interleaved groups of splits in parallel, each group in split order, then
-// the groups in order -- adds the residual if any, rounds and stores.
-template <typename T, int NB, int NW>
-__device__ __forceinline__ void down_finish(const float (&acc)[NB][vec16<T>::N],
-                                            float (&red)[NW][NB][64 * vec16<T>::N], int *s_last, int sl, int s,
-                                            int B, int d, int S, float *__restrict__ part, const T *residual,
-                                            T *out, uint32_t *slice_counter)
+// the groups in order -- multiplies by the output row's FP8 scale if any
+// (dsc), adds the residual if any, rounds and stores.  V: columns per lane.
+template <typename T, int V, int NB, int NW>
+__device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&red)[NW][NB][64 * V], int *s_last,
+                                            int sl, int s, int B, int d, int S, float *__restrict__ part,
+                                            const float *__restrict__ dsc, const T *residual, T *out,
+                                            uint32_t *slice_counter)
 {
     constexpr int NT = 64 * NW;
-    constexpr int V = vec16<T>::N;
     constexpr int COLS = 64 * V;
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
 #pragma unroll
@@ -261,19 +337,21 @@ __device__ __forceinline__ void down_finish(const float (&acc)[NB][vec16<T>::N],
         float y = gsum[0][b][ci];
 #pragma unroll
         for (int g = 1; g < GROUPS; ++g) y += gsum[g][b][ci];
+        if (dsc) y *= dsc[col];
         if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
         elem<T>::store(out, (int64_t)b * d + col, y);
     }
 }
 
-template <typename T, int NB, int NW>
+template <typename T, typename TW, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__ s_sp, int B, int k,
-                                                       const T *__restrict__ wdt, const int32_t *__restrict__ sel,
-                                                       int d, int F, int S, float *__restrict__ part,
-                                                       const T *residual, T *out, uint32_t *__restrict__ counters)
+                                                       const TW *__restrict__ wdt, const float *__restrict__ dsc,
+                                                       const int32_t *__restrict__ sel, int d, int F, int S,
+                                                       float *__restrict__ part, const T *residual, T *out,
+                                                       uint32_t *__restrict__ counters)
 {
     constexpr int NT = 64 * NW;
-    constexpr int V = vec16<T>::N;
+    constexpr int V = WRows<TW>::DV;
     constexpr int COLS = 64 * V;
     constexpr int U = kDownRowsPerWave;
     __shared__ float red[NW][NB][COLS];
@@ -298,17 +376,17 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[b][q] = 0.0f;
     if (nr > 0) {
-        u32x4 w[U];
+        typename WRows<TW>::dvec w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = __builtin_amdgcn_readlane(jl, u);
-            if (u < nr) w[u] = ld_stream(wdt + (int64_t)j * d + cc);
+            if (u < nr) w[u] = WRows<TW>::dload(wdt + (int64_t)j * d + cc);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (u < nr) {
                 float f[V];
-                vec16<T>::unpack(w[u], f);
+                WRows<TW>::dunpack(w[u], f);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const float sv = (b < B) ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sl_v[b]), u)) : 0.0f;
@@ -319,7 +397,7 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
         }
     }
 
-    down_finish<T, NB, NW>(acc, red, &s_last, sl, s, B, d, S, part, residual, out, &counters[sl]);
+    down_finish<T, V, NB, NW>(acc, red, &s_last, sl, s, B, d, S, part, dsc, residual, out, &counters[sl]);
 }
 
 // ------------------------------------------------------------------------
@@ -358,21 +436,21 @@ __device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target)
     return true;
 }
 
-template <typename T>
+template <typename T, typename TW>
 __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
-    const T *__restrict__ x, int d, int F, const T *__restrict__ w_gu, const T *__restrict__ wdt,
-    const int32_t *__restrict__ sel, int k, int n_gu, int n_slices, int S, float *__restrict__ s_sp,
-    float *__restrict__ part, const T *residual, T *out, uint32_t *__restrict__ counters,
-    int32_t *__restrict__ iota_out)
+    const T *__restrict__ x, int d, int F, const TW *__restrict__ w_gu, const float *__restrict__ gsc,
+    const TW *__restrict__ wdt, const float *__restrict__ dsc, const int32_t *__restrict__ sel, int k, int n_gu,
+    int n_slices, int S, float *__restrict__ s_sp, float *__restrict__ part, const T *residual, T *out,
+    uint32_t *__restrict__ counters, int32_t *__restrict__ iota_out)
 {
-    constexpr int V = vec16<T>::N;
+    constexpr int V = WRows<TW>::DV;
     constexpr int COLS = 64 * V;
     extern __shared__ float dyn[];  // gate/up: x [d]; down: red [kS2Waves][1][COLS]
     __shared__ int s_flag;
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
 
     if ((int)blockIdx.x < n_gu) {
-        gateup_block<T, 1, true>(x, 1, d, F, w_gu, sel, k, s_sp, iota_out, dyn, blockIdx.x);
+        gateup_block<T, TW, 1, true>(x, 1, d, F, w_gu, gsc, sel, k, s_sp, iota_out, dyn, blockIdx.x);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's s stores have completed
         __syncthreads();
         if (tid == 0)
@@ -409,25 +487,25 @@ __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
 #pragma unroll
     for (int q = 0; q < V; ++q) acc[0][q] = 0.0f;
     if (nr > 0) {
-        u32x4 w[kS2Rows];
+        typename WRows<TW>::dvec w[kS2Rows];
 #pragma unroll
         for (int u = 0; u < kS2Rows; ++u) {
             const int j = __builtin_amdgcn_readlane(jl, u);
-            if (u < nr) w[u] = ld_stream(wdt + (int64_t)j * d + cc);
+            if (u < nr) w[u] = WRows<TW>::dload(wdt + (int64_t)j * d + cc);
         }
 #pragma unroll
         for (int u = 0; u < kS2Rows; ++u) {
             if (u < nr) {
                 float f[V];
-                vec16<T>::unpack(w[u], f);
+                WRows<TW>::dunpack(w[u], f);
                 const float sv = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sv_l), u));
 #pragma unroll
                 for (int q = 0; q < V; ++q) acc[0][q] = fmaf(sv, f[q], acc[0][q]);
             }
         }
     }
-    down_finish<T, 1, kS2Waves>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d, S,
-                                part, residual, out, &counters[kDownSliceBase + sl]);
+    down_finish<T, V, 1, kS2Waves>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d,
+                                   S, part, dsc, residual, out, &counters[kDownSliceBase + sl]);
 }
 
 // out = residual (or 0): the k == 0 case
@@ -468,43 +546,50 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *h, int d, float e
 // ------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------
-template <typename T>
-static hipError_t gateup_t(const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel, int k, float *s_sp,
-                           int32_t *iota_out, hipStream_t st)
+template <typename T, typename TW>
+static hipError_t gateup_t(const void *x, int B, int d, int F, const S2Weights &w, const int32_t *sel, int k,
+                           float *s_sp, int32_t *iota_out, hipStream_t st)
 {
     if (k <= 0) return hipSuccess;
     const int blocks = (k + 3) / 4;  // one channel per wave
     // x of up to 4 tokens staged in LDS as fp32, within 64 KB
     const int tb = (4 * d * (int)sizeof(float) <= 65536) ? 4 : 1;
+    const TW *wgu = (const TW *)w.w_gu;
     for (int b0 = 0; b0 < B; b0 += tb) {
         const int nb = (B - b0 >= tb) ? tb : B - b0;
         const T *xp = (const T *)x + (int64_t)b0 * d;
         float *sp = s_sp + (int64_t)b0 * k;
         int32_t *io = (b0 == 0) ? iota_out : nullptr;
         if (nb == 1)
-            gateup_kernel<T, 1><<<blocks, 256, d * sizeof(float), st>>>(xp, 1, d, F, (const T *)w_gu, sel, k, sp, io);
+            gateup_kernel<T, TW, 1><<<blocks, 256, xpad_row<gu_xpad<TW, 1>()>(d) * sizeof(float), st>>>(
+                xp, 1, d, F, wgu, w.gu_scales, sel, k, sp, io);
         else
-            gateup_kernel<T, 4><<<blocks, 256, 4 * d * sizeof(float), st>>>(xp, nb, d, F, (const T *)w_gu, sel, k, sp, io);
+            gateup_kernel<T, TW, 4><<<blocks, 256, 4 * d * sizeof(float), st>>>(xp, nb, d, F, wgu, w.gu_scales,
+                                                                                sel, k, sp, io);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t launch_gateup(int dtype, const void *x, int B, int d, int F, const void *w_gu, const int32_t *sel,
+hipError_t launch_gateup(int dtype, const S2Weights &w, const void *x, int B, int d, int F, const int32_t *sel,
                          int k, float *s_sp, int32_t *iota_out, hipStream_t st)
 {
-    return dtype == 0 ? gateup_t<float>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, st)
-                      : gateup_t<uint16_t>(x, B, d, F, w_gu, sel, k, s_sp, iota_out, st);
+    if (w.fmt == 1)
+        return dtype == 0 ? gateup_t<float, uint8_t>(x, B, d, F, w, sel, k, s_sp, iota_out, st)
+                          : gateup_t<uint16_t, uint8_t>(x, B, d, F, w, sel, k, s_sp, iota_out, st);
+    return dtype == 0 ? gateup_t<float, float>(x, B, d, F, w, sel, k, s_sp, iota_out, st)
+                      : gateup_t<uint16_t, uint16_t>(x, B, d, F, w, sel, k, s_sp, iota_out, st);
 }
 
-template <typename T>
-static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, const void *wdt, const int32_t *sel,
-                         int d, int F, float *part, const void *residual, void *out, uint32_t *counters,
-                         hipStream_t st)
+template <typename T, typename TW>
+static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, const S2Weights &w,
+                         const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
+                         uint32_t *counters, hipStream_t st)
 {
     dim3 grid(pl.n_slices, pl.S);
     dim3 grid4(pl.n_slices, 2 * pl.S);  // half-size workgroups for 4-token passes
+    const TW *wdt = (const TW *)w.w_down_t;
     // tokens in passes of at most 4 (a pass re-reads the selected rows)
     for (int b0 = 0; b0 < B; b0 += 4) {
         const int nb = (B - b0 >= 4) ? 4 : B - b0;
@@ -512,46 +597,61 @@ static hipError_t down_t(const DownPlan &pl, const float *s_sp, int B, int k, co
         const T *res = residual ? (const T *)residual + (int64_t)b0 * d : nullptr;
         T *o = (T *)out + (int64_t)b0 * d;
         if (nb == 1)
-            down_kernel<T, 1, kDownWaves><<<grid, 64 * kDownWaves, 0, st>>>(sp, 1, k, (const T *)wdt, sel, d, F, pl.S,
-                                                                         part, res, o, counters);
+            down_kernel<T, TW, 1, kDownWaves><<<grid, 64 * kDownWaves, 0, st>>>(
+                sp, 1, k, wdt, w.down_scales, sel, d, F, pl.S, part, res, o, counters);
         else
-            down_kernel<T, 4, kDownWaves / 2><<<grid4, 32 * kDownWaves, 0, st>>>(sp, nb, k, (const T *)wdt, sel, d, F,
-                                                                              2 * pl.S, part, res, o, counters);
+            down_kernel<T, TW, 4, kDownWaves / 2><<<grid4, 32 * kDownWaves, 0, st>>>(
+                sp, nb, k, wdt, w.down_scales, sel, d, F, 2 * pl.S, part, res, o, counters);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t launch_down(int dtype, const DownPlan &pl, const float *s_sp, int B, int k, const void *w_down_t,
+hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const float *s_sp, int B, int k,
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st)
 {
-    return dtype == 0 ? down_t<float>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st)
-                      : down_t<uint16_t>(pl, s_sp, B, k, w_down_t, sel, d, F, part, residual, out, counters, st);
+    if (w.fmt == 1)
+        return dtype == 0 ? down_t<float, uint8_t>(pl, s_sp, B, k, w, sel, d, F, part, residual, out, counters, st)
+                          : down_t<uint16_t, uint8_t>(pl, s_sp, B, k, w, sel, d, F, part, residual, out, counters,
+                                                      st);
+    return dtype == 0 ? down_t<float, float>(pl, s_sp, B, k, w, sel, d, F, part, residual, out, counters, st)
+                      : down_t<uint16_t, uint16_t>(pl, s_sp, B, k, w, sel, d, F, part, residual, out, counters, st);
 }
 
-hipError_t launch_stage2_fused(int dtype, const void *x, int d, int F, const void *w_gu, const void *w_down_t,
-                               const int32_t *sel, int k, float *s_sp, float *part, const void *residual, void *out,
-                               uint32_t *counters, int32_t *iota_out, hipStream_t st)
+template <typename T, typename TW>
+static hipError_t stage2_fused_t(const void *x, int d, int F, const S2Weights &w, const int32_t *sel, int k,
+                                 float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
+                                 int32_t *iota_out, hipStream_t st)
 {
-    if (k <= 0) return hipErrorInvalidValue;
-    const int V = dtype == 0 ? 4 : 8;
+    constexpr int V = WRows<TW>::DV;
     const int n_gu = (k + 3) / 4;
     const int n_slices = (d + 64 * V - 1) / (64 * V);
     const int S = (k + kS2Ranks - 1) / kS2Ranks;
     if (S > kS2MaxSplits || n_slices > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
     const dim3 grid(n_gu + n_slices * S);
-    const size_t lds = sizeof(float) * (size_t)max(d, kS2Waves * 64 * V);
-    if (dtype == 0)
-        stage2_fused_kernel<float><<<grid, 64 * kS2Waves, lds, st>>>(
-            (const float *)x, d, F, (const float *)w_gu, (const float *)w_down_t, sel, k, n_gu, n_slices, S, s_sp,
-            part, (const float *)residual, (float *)out, counters, iota_out);
-    else
-        stage2_fused_kernel<uint16_t><<<grid, 64 * kS2Waves, lds, st>>>(
-            (const uint16_t *)x, d, F, (const uint16_t *)w_gu, (const uint16_t *)w_down_t, sel, k, n_gu, n_slices, S,
-            s_sp, part, (const uint16_t *)residual, (uint16_t *)out, counters, iota_out);
+    const size_t lds = sizeof(float) * (size_t)max(xpad_row<gu_xpad<TW, 1>()>(d), kS2Waves * 64 * V);
+    stage2_fused_kernel<T, TW><<<grid, 64 * kS2Waves, lds, st>>>(
+        (const T *)x, d, F, (const TW *)w.w_gu, w.gu_scales, (const TW *)w.w_down_t, w.down_scales, sel, k, n_gu,
+        n_slices, S, s_sp, part, (const T *)residual, (T *)out, counters, iota_out);
     return hipGetLastError();
+}
+
+hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int d, int F, const int32_t *sel, int k,
+                               float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
+                               int32_t *iota_out, hipStream_t st)
+{
+    if (k <= 0) return hipErrorInvalidValue;
+    if (w.fmt == 1)
+        return dtype == 0 ? stage2_fused_t<float, uint8_t>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
+                                                           iota_out, st)
+                          : stage2_fused_t<uint16_t, uint8_t>(x, d, F, w, sel, k, s_sp, part, residual, out,
+                                                              counters, iota_out, st);
+    return dtype == 0 ? stage2_fused_t<float, float>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
+                                                     iota_out, st)
+                      : stage2_fused_t<uint16_t, uint16_t>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
+                                                           iota_out, st);
 }
 
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st)

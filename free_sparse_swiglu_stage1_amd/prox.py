@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libprox.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 Q_INT8_ROW, Q_INT4_G128 = 0, 1
+W_NATIVE, W_FP8_E4M3 = 0, 1
 MODES = {"int8_row": Q_INT8_ROW, "int4_g128": Q_INT4_G128}
 
 SYMBOLS = (
-    "prox_status_string", "prox_version", "prox_counts", "prox_pack_weights", "prox_proxy_sizes",
+    "prox_status_string", "prox_version", "prox_counts", "prox_pack_weights", "prox_pack_weights_fp8",
+    "prox_proxy_sizes",
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
 )
@@ -37,7 +39,8 @@ class ProxError(RuntimeError):
 
 class _CWeights(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64), ("dtype", ctypes.c_int),
-                ("w_gu", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p)]
+                ("w_gu", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p), ("wformat", ctypes.c_int),
+                ("gu_scales", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
 
 
 class _CProxy(ctypes.Structure):
@@ -67,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         "prox_version": ([], ctypes.c_char_p),
         "prox_counts": ([I64, I64, F, F, PI, PI], I32),
         "prox_pack_weights": ([P, P, P, I64, I64, I32, P, P, P], I32),
+        "prox_pack_weights_fp8": ([P, P, P, I64, I64, I32, P, P, P, P, P], I32),
         "prox_proxy_sizes": ([I64, I64, I32, PS, PS], I32),
         "prox_quantize_proxy": ([PW, I32, P, P, P], I32),
         "prox_workspace_size": ([I64, I64, I64, I32, PS], I32),
@@ -119,15 +123,27 @@ def _dev(t: torch.Tensor, name: str):
 
 @dataclass
 class Weights:
-    """Full-precision weights in the library's channel-major layout."""
+    """Exact weights in the library's channel-major layout: in the activation
+    dtype, or FP8 E4M3 codes (uint8) with per-row scales."""
     w_gu: torch.Tensor        # [F][2][d]
     w_down_t: torch.Tensor    # [F][d]
     d_model: int
     d_ff: int
+    act_dtype: torch.dtype = None            # x / out dtype (default: the weights' dtype)
+    gu_scales: torch.Tensor = None           # FP8: fp32 [F][2]
+    down_scales: torch.Tensor = None         # FP8: fp32 [d]
+
+    @property
+    def fp8(self) -> bool:
+        return self.gu_scales is not None
 
     def c(self) -> _CWeights:
-        return _CWeights(self.d_model, self.d_ff, _dtype_code(self.w_gu.dtype), self.w_gu.data_ptr(),
-                         self.w_down_t.data_ptr())
+        dt = self.act_dtype if self.act_dtype is not None else self.w_gu.dtype
+        if self.fp8:
+            return _CWeights(self.d_model, self.d_ff, _dtype_code(dt), self.w_gu.data_ptr(), self.w_down_t.data_ptr(),
+                             W_FP8_E4M3, self.gu_scales.data_ptr(), self.down_scales.data_ptr())
+        return _CWeights(self.d_model, self.d_ff, _dtype_code(dt), self.w_gu.data_ptr(), self.w_down_t.data_ptr(),
+                         W_NATIVE, None, None)
 
 
 @dataclass
@@ -168,6 +184,25 @@ def pack_weights(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor)
     _check(lib.prox_pack_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), d, F, _dtype_code(w_gate.dtype),
                                  _ptr(w_gu), _ptr(w_dt), _stream(w_gate.device)), "prox_pack_weights")
     return Weights(w_gu, w_dt, d, F)
+
+
+def pack_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor) -> Weights:
+    """nn.Linear weights -> FP8 E4M3 codes in the channel-major layout, one fp32
+    scale per output row; activations keep w_gate's dtype."""
+    lib = load_library()
+    F, d = w_gate.shape
+    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _dev(t, n)
+    assert w_up.shape == (F, d) and w_down.shape == (d, F)
+    dev = w_gate.device
+    w_gu = torch.empty((F, 2, d), dtype=torch.uint8, device=dev)
+    w_dt = torch.empty((F, d), dtype=torch.uint8, device=dev)
+    gsc = torch.empty((F, 2), dtype=torch.float32, device=dev)
+    dsc = torch.empty((d,), dtype=torch.float32, device=dev)
+    _check(lib.prox_pack_weights_fp8(_ptr(w_gate), _ptr(w_up), _ptr(w_down), d, F, _dtype_code(w_gate.dtype),
+                                     _ptr(w_gu), _ptr(gsc), _ptr(w_dt), _ptr(dsc), _stream(dev)),
+           "prox_pack_weights_fp8")
+    return Weights(w_gu, w_dt, d, F, act_dtype=w_gate.dtype, gu_scales=gsc, down_scales=dsc)
 
 
 def proxy_sizes(d: int, F: int, mode: str):

@@ -65,16 +65,34 @@ typedef enum { PROX_F32 = 0, PROX_BF16 = 1 } prox_dtype;
  * [-7,7]. */
 typedef enum { PROX_Q_INT8_ROW = 0, PROX_Q_INT4_G128 = 1 } prox_qmode;
 
-/* Full-precision weights in the library's channel-major layout (produced by
- * prox_pack_weights):
+/* Storage of the exact weights Stage 2 reads.  The pages say Prox composes
+ * with FP8 model quantization (technical summary, Experimental Results and
+ * Significance and Claims) without fixing a scheme.  PROX_W_FP8_E4M3 is OCP
+ * E4M3 (bias 7, largest finite 448) with one fp32 scale per output row:
+ * scale = fl32(amax / 448), code = nearest E4M3 value to fl32(w / scale),
+ * ties to the even code, saturating; an all-zero row has scale 0.  Weight
+ * value = scale * decode(code).  Activations and accumulation are unchanged. */
+typedef enum { PROX_W_NATIVE = 0, PROX_W_FP8_E4M3 = 1 } prox_wformat;
+
+/* Exact weights in the library's channel-major layout (produced by
+ * prox_pack_weights, or prox_pack_weights_fp8):
  *   w_gu     [F][2][d]  row j*2 = gate row j, row j*2+1 = up row j, so the two
  *                       rows a selected channel needs are one contiguous run;
- *   w_down_t [F][d]     = W_down^T: row j holds the d outputs channel j feeds. */
+ *   w_down_t [F][d]     = W_down^T: row j holds the d outputs channel j feeds.
+ * dtype is the type of x and out, and of the weights when wformat is
+ * PROX_W_NATIVE.  With PROX_W_FP8_E4M3 both arrays hold E4M3 codes (one byte
+ * each), gu_scales [F][2] holds the scales of gate row j and up row j, and
+ * down_scales [d] the scale of W_down's row m (column m of w_down_t); the
+ * FP8 path needs d % 16 == 0.  A zero-filled tail (wformat 0, NULL scales)
+ * is the native layout. */
 typedef struct {
     int64_t d_model, d_ff;
     prox_dtype dtype;
-    const void *w_gu;     /* device */
-    const void *w_down_t; /* device */
+    const void *w_gu;          /* device */
+    const void *w_down_t;      /* device */
+    prox_wformat wformat;
+    const float *gu_scales;    /* device, FP8 only */
+    const float *down_scales;  /* device, FP8 only */
 } prox_weights;
 
 /* Quantized proxy of W_gate and W_up (produced by prox_quantize_proxy).
@@ -118,6 +136,19 @@ prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *
                               int64_t d_model, int64_t d_ff, prox_dtype dtype,
                               void *w_gu_out, void *w_down_t_out, hipStream_t stream);
 
+/* Offline: FP8 (E4M3) copy of nn.Linear weights in the same layout, with the
+ * scales described at prox_wformat.
+ *   w_gate, w_up [F][d], w_down [d][F] (device, row-major, dtype, finite)
+ *   w_gu_out uint8 [F][2][d], gu_scales_out fp32 [F][2],
+ *   w_down_t_out uint8 [F][d], down_scales_out fp32 [d] (device; caller-allocated)
+ * d % 16 == 0, else PROX_ERR_UNSUPPORTED.  Inputs and outputs must not
+ * overlap.  Fill a prox_weights with wformat = PROX_W_FP8_E4M3, these four
+ * outputs, and dtype = the activations' type. */
+prox_status prox_pack_weights_fp8(const void *w_gate, const void *w_up, const void *w_down,
+                                  int64_t d_model, int64_t d_ff, prox_dtype dtype,
+                                  void *w_gu_out, float *gu_scales_out, void *w_down_t_out,
+                                  float *down_scales_out, hipStream_t stream);
+
 /* Bytes of the proxy buffers for a shape and mode (host-only). */
 prox_status prox_proxy_sizes(int64_t d_model, int64_t d_ff, prox_qmode mode,
                              size_t *codes_bytes, size_t *scales_bytes);
@@ -128,6 +159,7 @@ prox_status prox_proxy_sizes(int64_t d_model, int64_t d_ff, prox_qmode mode,
  * channel's 128-input group for INT4_G128): a = max |w| (binary32),
  * scale = a / qmax rounded to binary32, q = clamp(rint(w / scale)) with
  * round-to-nearest-even binary32 division; a == 0 gives scale 0 and q 0.
+ * With FP8 weights, w is the binary32 value fl32(scale * decode(code)).
  * codes, scales: device buffers of prox_proxy_sizes() bytes. */
 prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *codes, void *scales,
                                 hipStream_t stream);

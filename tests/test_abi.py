@@ -97,8 +97,8 @@ def test_workspace_size_limits():
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: validation fails first
 
 
-def _w(d=4096, F=14336, dtype=B.BF16, gu=FAKE, dt=FAKE + 4096):
-    return B._CWeights(d, F, dtype, gu, dt)
+def _w(d=4096, F=14336, dtype=B.BF16, gu=FAKE, dt=FAKE + 4096, wformat=B.W_NATIVE, gsc=None, dsc=None):
+    return B._CWeights(d, F, dtype, gu, dt, wformat, gsc, dsc)
 
 
 def _p(d=4096, F=14336, mode=B.Q_INT8_ROW, codes=FAKE + 8192, scales=FAKE + 12288):
@@ -135,6 +135,11 @@ def _fwd(lib, x=FAKE + 16384, batch=1, w=None, p=None, keep=0.5, sp=0.7, out=FAK
     (dict(p=_p(mode=5)), B.ERR_UNSUPPORTED),
     (dict(p=_p(codes=FAKE + 1)), B.ERR_INVALID_ARG),
     (dict(p=_p(mode=B.Q_INT4_G128), batch=8), B.ERR_UNSUPPORTED),
+    (dict(w=_w(wformat=7)), B.ERR_UNSUPPORTED),
+    (dict(w=_w(wformat=B.W_FP8_E4M3)), B.ERR_INVALID_ARG),                       # FP8 without scales
+    (dict(w=_w(wformat=B.W_FP8_E4M3, gsc=FAKE + 40960, dsc=FAKE + 8)), B.ERR_INVALID_ARG),  # misaligned
+    (dict(w=_w(d=4104, wformat=B.W_FP8_E4M3, gsc=FAKE + 40960, dsc=FAKE + 45056),
+          p=_p(d=4104)), B.ERR_UNSUPPORTED),                                     # FP8 needs d % 16 == 0
 ])
 def test_forward_rejects_before_launch(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -158,6 +163,11 @@ def test_other_entry_points_reject(lib):
     assert lib.prox_pack_weights(v(FAKE), v(FAKE), v(0), 4096, 14336, B.BF16, v(FAKE), v(FAKE),
                                  None) == B.ERR_INVALID_ARG
     assert lib.prox_quantize_proxy(ctypes.byref(w), 3, v(FAKE), v(FAKE), None) == B.ERR_UNSUPPORTED
+    f8 = (v(FAKE), v(FAKE + 64), v(FAKE + 128), v(FAKE + 192))
+    assert lib.prox_pack_weights_fp8(v(FAKE), v(FAKE), v(FAKE), 4104, 14336, B.BF16, *f8, None) == B.ERR_UNSUPPORTED
+    assert lib.prox_pack_weights_fp8(v(FAKE), v(FAKE), v(FAKE), 4096, 14336, 5, *f8, None) == B.ERR_UNSUPPORTED
+    assert lib.prox_pack_weights_fp8(v(FAKE), v(FAKE), v(FAKE), 4096, 14336, B.BF16, v(FAKE), None, v(FAKE),
+                                     v(FAKE), None) == B.ERR_INVALID_ARG
     ws = (B._CWeights * 2)(w, _w(F=11008))
     ps = (B._CProxy * 2)(p, _p(F=11008))
     assert lib.prox_chain_forward(v(FAKE), 1, ws, ps, 2, 1e-5, 0.5, 0.7, v(FAKE + 256), 1 << 40,
