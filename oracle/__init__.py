@@ -30,6 +30,10 @@ _LIB = os.path.join(_HERE, "libprox_oracle.so")
 MODE_INT8_ROW = 0
 MODE_INT4_G128 = 1
 _MODES = {"int8_row": MODE_INT8_ROW, "int4_g128": MODE_INT4_G128}
+ACTS = {"silu": 0, "gelu_tanh": 1}
+# selection signals: the proxy intermediate state (Prox), one proxy branch,
+# or the exact intermediate state (dense exact gate/up: the "oracle" mask)
+SIGNALS = {"s": 0, "h": 1, "u": 2, "exact_s": 3}
 
 _lib = None
 
@@ -69,6 +73,8 @@ def _bind(lib):
     D = ctypes.c_double
     lib.oracle_silu.argtypes = [D]
     lib.oracle_silu.restype = D
+    lib.oracle_gelu_tanh.argtypes = [D]
+    lib.oracle_gelu_tanh.restype = D
     lib.oracle_input_count.argtypes = [D, I]
     lib.oracle_input_count.restype = I
     lib.oracle_channel_count.argtypes = [D, I]
@@ -77,8 +83,8 @@ def _bind(lib):
     lib.oracle_quantize_int4_g128.argtypes = [P, I, I, P, P]
     lib.oracle_topk_ascending.argtypes = [P, I, I, P, P]
     lib.oracle_input_select.argtypes = [P, I, I, I, P]
-    lib.oracle_proxy.argtypes = [P, I, I, I, ctypes.c_int, P, P, P, P, P, P, P]
-    lib.oracle_ffn_masked.argtypes = [P, I, I, I, P, P, P, P, I, P, P]
+    lib.oracle_proxy.argtypes = [P, I, I, I, ctypes.c_int, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P, P]
+    lib.oracle_ffn_masked.argtypes = [P, I, I, I, P, P, P, P, I, ctypes.c_int, P, P]
     lib.oracle_rmsnorm.argtypes = [P, I, I, D, P]
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_int]
     lib.oracle_e4m3_decode.restype = D
@@ -86,7 +92,7 @@ def _bind(lib):
     lib.oracle_e4m3_encode.restype = ctypes.c_int
     lib.oracle_quantize_fp8_row.argtypes = [P, I, I, P, P]
     lib.oracle_dequant_fp8_f32.argtypes = [P, P, I, I, P]
-    lib.oracle_ffn_masked_fp8.argtypes = [P, I, I, I, P, P, P, P, P, P, P, I, P, P]
+    lib.oracle_ffn_masked_fp8.argtypes = [P, I, I, I, P, P, P, P, P, P, P, I, ctypes.c_int, P, P]
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -117,6 +123,10 @@ def get_threads() -> int:
 
 
 # ---------------------------------------------------------------- steps
+
+def gelu_tanh(z: float) -> float:
+    return _load().oracle_gelu_tanh(float(z))
+
 
 def silu(z: float) -> float:
     return float(_load().oracle_silu(float(z)))
@@ -182,7 +192,7 @@ def dequant_fp8_f32(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
     return w
 
 
-def ffn_masked_fp8(x: np.ndarray, fp8, sel: np.ndarray):
+def ffn_masked_fp8(x: np.ndarray, fp8, sel: np.ndarray, act: str = "silu"):
     """Stage-2 exact SwiGLU on FP8 weights, fp8 = (qg, sg, qu, su, qd, sd) from
     ``quantize_fp8`` of W_gate, W_up [F][d] and W_down [d][F].
 
@@ -198,7 +208,7 @@ def ffn_masked_fp8(x: np.ndarray, fp8, sel: np.ndarray):
     y = np.empty((B, d))
     s = np.empty((B, k))
     _load().oracle_ffn_masked_fp8(_p(x), B, d, F, _p(qg), _p(sg), _p(qu), _p(su), _p(qd), _p(sd), _p(sel), k,
-                                  _p(s), _p(y))
+                                  ACTS[act], _p(s), _p(y))
     return y, s
 
 
@@ -220,8 +230,9 @@ def input_select(x: np.ndarray, k_in: int) -> np.ndarray:
     return xh
 
 
-def proxy(xhat: np.ndarray, qg, scg, qu, scu, mode: str):
-    """Proxy gate/up activations and the channel salience score.
+def proxy(xhat: np.ndarray, qg, scg, qu, scu, mode: str, act: str = "silu", signal: str = "s"):
+    """Proxy gate/up activations and the channel salience score for a proxy
+    signal ("s": |act(g~) u~|, "h": |act(g~)|, "u": |u~|), summed over tokens.
 
     Returns (g~ [B][F], u~ [B][F], score [F])."""
     xhat = np.ascontiguousarray(np.atleast_2d(xhat), dtype=np.float64)
@@ -235,11 +246,11 @@ def proxy(xhat: np.ndarray, qg, scg, qu, scu, mode: str):
     ut = np.empty((B, F))
     score = np.empty((F,))
     _load().oracle_proxy(_p(xhat), B, d, F, _MODES[mode], _p(qg), _p(scg), _p(qu), _p(scu),
-                         _p(gt), _p(ut), _p(score))
+                         ACTS[act], SIGNALS[signal], _p(gt), _p(ut), _p(score))
     return gt, ut, score
 
 
-def ffn_masked(x: np.ndarray, wg, wu, wd, sel: np.ndarray):
+def ffn_masked(x: np.ndarray, wg, wu, wd, sel: np.ndarray, act: str = "silu"):
     """Stage-2 exact SwiGLU FFN on the channels in ``sel`` (ascending).
 
     Returns (y [B][d] binary64, s [B][k])."""
@@ -252,14 +263,23 @@ def ffn_masked(x: np.ndarray, wg, wu, wd, sel: np.ndarray):
     k = sel.size
     y = np.empty((B, d))
     s = np.empty((B, k))
-    _load().oracle_ffn_masked(_p(x), B, d, F, _p(wg), _p(wu), _p(wd), _p(sel), k, _p(s), _p(y))
+    _load().oracle_ffn_masked(_p(x), B, d, F, _p(wg), _p(wu), _p(wd), _p(sel), k, ACTS[act], _p(s), _p(y))
     return y, s
 
 
-def ffn_dense(x, wg, wu, wd):
-    """Dense SwiGLU FFN: the masked FFN with every channel selected."""
+def ffn_dense(x, wg, wu, wd, act: str = "silu"):
+    """Dense SwiGLU (or GeGLU) FFN: the masked FFN with every channel selected."""
     F = np.asarray(wg).shape[0]
-    return ffn_masked(x, wg, wu, wd, np.arange(F, dtype=np.int64))
+    return ffn_masked(x, wg, wu, wd, np.arange(F, dtype=np.int64), act)
+
+
+def exact_scores(x, wg, wu, wd, act: str = "silu", fp8=None):
+    """The exact-state signal, score_j = sum_b |s_{b,j}| with s the exact
+    intermediate state of every channel (dense x, the exact weights)."""
+    F = (np.asarray(wg) if fp8 is None else fp8[0]).shape[0]
+    allc = np.arange(F, dtype=np.int64)
+    _, s = ffn_masked(x, wg, wu, wd, allc, act) if fp8 is None else ffn_masked_fp8(x, fp8, allc, act)
+    return np.abs(s).sum(axis=0)
 
 
 def rmsnorm(h: np.ndarray, eps: float = 1e-5) -> np.ndarray:
@@ -272,14 +292,18 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-5) -> np.ndarray:
 
 # --------------------------------------------------------- whole forward
 
-def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float, mode: str, fp8=None):
+def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float, mode: str, fp8=None,
+                 act: str = "silu", signal: str = "s"):
     """The Prox forward, step by step.
 
     proxy_q = (codes_gate, scales_gate, codes_up, scales_up) from ``quantize``.
     Stage 1: sparse x -> proxy g~, u~ -> salience -> top-k mask (shared by
     gate, up and down).  Stage 2: exact masked SwiGLU with dense x; with
     ``fp8`` = (qg, sg, qu, su, qd, sd), on those FP8 weights instead of
-    wg, wu, wd (which may then be None).
+    wg, wu, wd (which may then be None).  ``act`` is the gate activation
+    (silu, or gelu_tanh for GeGLU FFNs); ``signal`` the selection signal:
+    "s" (Prox), "h" or "u" (one proxy branch), or "exact_s" (the exact
+    intermediate state of every channel, no proxy: the ideal mask).
     Returns a dict with k_in, k, xhat, score, sel, T (k-th score), y, s."""
     x = np.atleast_2d(x)
     B, d = x.shape
@@ -287,10 +311,14 @@ def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float,
     k_in = input_count(input_keep, d)
     k = channel_count(ffn_sparsity, F)
     xhat = input_select(x, k_in)
-    qg, scg, qu, scu = proxy_q
-    gt, ut, score = proxy(xhat, qg, scg, qu, scu, mode)
+    if signal == "exact_s":
+        gt = ut = None
+        score = exact_scores(x, wg, wu, wd, act, fp8)
+    else:
+        qg, scg, qu, scu = proxy_q
+        gt, ut, score = proxy(xhat, qg, scg, qu, scu, mode, act, signal)
     sel, T = topk_ascending(score, k)
-    y, s = ffn_masked(x, wg, wu, wd, sel) if fp8 is None else ffn_masked_fp8(x, fp8, sel)
+    y, s = ffn_masked(x, wg, wu, wd, sel, act) if fp8 is None else ffn_masked_fp8(x, fp8, sel, act)
     return dict(k_in=k_in, k=k, xhat=xhat, g_proxy=gt, u_proxy=ut, score=score, sel=sel, T=T, y=y, s=s)
 
 

@@ -59,6 +59,20 @@ double oracle_silu(double z)
     return z / (1.0 + exp(-z));
 }
 
+/* GELU-gated FFNs (GeGLU) in the tanh form of the Gemma family the pages */
+/* also evaluate (technical summary, Key Contributions: Gemma-3 among the */
+/* six families): gelu(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))). */
+double oracle_gelu_tanh(double z)
+{
+    return 0.5 * z * (1.0 + tanh(sqrt(2.0 / acos(-1.0)) * (z + 0.044715 * z * z * z)));
+}
+
+/* the gate activation h = act(g): 0 = silu (SwiGLU), 1 = gelu_tanh (GeGLU) */
+double oracle_act(int act, double z)
+{
+    return act == 1 ? oracle_gelu_tanh(z) : oracle_silu(z);
+}
+
 /* ------------------------------------------------------------------ */
 /* Counts.  The pages give input sparsity as a fraction of retained    */
 /* input entries (Sparsity Allocation: keep at least 30%) and Stage-2  */
@@ -209,9 +223,22 @@ static double dequant(const int8_t *q, const float *scale, int mode, int64_t d, 
     return s * (double)q[j * d + i];
 }
 
+/* The per-token salience term of a channel for the selection signal.    */
+/* Problem Statement: the exact intermediate state s = u (.) h is the      */
+/* ideal signal; prior methods use one branch, the gate activation h or    */
+/* the up activation u.  signal 0 = |h~ u~| (Prox), 1 = |h~| (gate branch  */
+/* only), 2 = |u~| (up branch only), with h~ = act(g~).                    */
+static double salience_term(int signal, int act, double g, double u)
+{
+    double h = oracle_act(act, g);
+    if (signal == 1) return fabs(h);
+    if (signal == 2) return fabs(u);
+    return fabs(h * u);
+}
+
 void oracle_proxy(const double *xhat, int64_t B, int64_t d, int64_t F, int mode,
                   const int8_t *qg, const float *scg, const int8_t *qu, const float *scu,
-                  double *gt, double *ut, double *score)
+                  int act, int signal, double *gt, double *ut, double *score)
 {
     int64_t j;
 #pragma omp parallel for schedule(static)
@@ -226,7 +253,7 @@ void oracle_proxy(const double *xhat, int64_t B, int64_t d, int64_t F, int mode,
             }
             gt[b * F + j] = g;
             ut[b * F + j] = u;
-            sc += fabs(oracle_silu(g) * u);
+            sc += salience_term(signal, act, g, u);
         }
         score[j] = sc;
     }
@@ -237,14 +264,14 @@ void oracle_proxy(const double *xhat, int64_t B, int64_t d, int64_t F, int mode,
 /* Output).  For each selected channel j, with the original weights and */
 /* the dense input x (reading: the proxy values and the sparsified x    */
 /* are not propagated downstream): g = W_gate[j] . x, u = W_up[j] . x,  */
-/* s = silu(g) * u; then y = sum over selected j of W_down[:, j] * s_j  */
+/* s = act(g) * u; then y = sum over selected j of W_down[:, j] * s_j   */
 /* (the down projection restricted to the same mask).                  */
 /* x: [B][d]; wg, wu: [F][d]; wd: [d][F] (nn.Linear orientation);       */
 /* sel: [k] ascending; s: [B][k] (nullable); y: [B][d].                */
 /* ------------------------------------------------------------------ */
 void oracle_ffn_masked(const double *x, int64_t B, int64_t d, int64_t F,
                        const float *wg, const float *wu, const float *wd,
-                       const int64_t *sel, int64_t k, double *s_out, double *y)
+                       const int64_t *sel, int64_t k, int act, double *s_out, double *y)
 {
     double *s = (double *)malloc((size_t)(B * k > 0 ? B * k : 1) * sizeof(double));
     int64_t r;
@@ -258,7 +285,7 @@ void oracle_ffn_masked(const double *x, int64_t B, int64_t d, int64_t F,
                 g += (double)wg[j * d + i] * xb[i];
                 u += (double)wu[j * d + i] * xb[i];
             }
-            s[b * k + r] = oracle_silu(g) * u;
+            s[b * k + r] = oracle_act(act, g) * u;
         }
     }
     int64_t m;
@@ -350,7 +377,7 @@ void oracle_dequant_fp8_f32(const uint8_t *q, const float *scale, int64_t rows, 
 /* nn.Linear orientation), scales [d].                                      */
 void oracle_ffn_masked_fp8(const double *x, int64_t B, int64_t d, int64_t F,
                            const uint8_t *qg, const float *sg, const uint8_t *qu, const float *su,
-                           const uint8_t *qd, const float *sd, const int64_t *sel, int64_t k,
+                           const uint8_t *qd, const float *sd, const int64_t *sel, int64_t k, int act,
                            double *s_out, double *y)
 {
     double *s = (double *)malloc((size_t)(B * k > 0 ? B * k : 1) * sizeof(double));
@@ -365,7 +392,7 @@ void oracle_ffn_masked_fp8(const double *x, int64_t B, int64_t d, int64_t F,
                 g += (double)sg[j] * oracle_e4m3_decode(qg[j * d + i]) * xb[i];
                 u += (double)su[j] * oracle_e4m3_decode(qu[j * d + i]) * xb[i];
             }
-            s[b * k + r] = oracle_silu(g) * u;
+            s[b * k + r] = oracle_act(act, g) * u;
         }
     }
     int64_t m;

@@ -23,8 +23,12 @@ MUTANTS = [
     ("tie goes to higher index", "return (a->idx < b->idx) ? -1 : (a->idx > b->idx) ? 1 : 0;",
      "return (a->idx < b->idx) ? 1 : (a->idx > b->idx) ? -1 : 0;"),
     ("up proxy reads gate codes", "u += xb[i] * dequant(qu, scu,", "u += xb[i] * dequant(qg, scg,"),
-    ("salience from gate only", "sc += fabs(oracle_silu(g) * u);", "sc += fabs(oracle_silu(g));"),
-    ("batch salience not summed", "sc += fabs(oracle_silu(g) * u);", "sc = fabs(oracle_silu(g) * u);"),
+    ("salience from gate only", "return fabs(h * u);", "return fabs(h);"),
+    ("batch salience not summed", "sc += salience_term(signal, act, g, u);", "sc = salience_term(signal, act, g, u);"),
+    ("gate signal reads up", "if (signal == 1) return fabs(h);", "if (signal == 1) return fabs(u);"),
+    ("up signal reads gate", "if (signal == 2) return fabs(u);", "if (signal == 2) return fabs(h);"),
+    ("gelu without the cubic term", "(z + 0.044715 * z * z * z)", "(z + 0.044715 * z * z)"),
+    ("activation choice ignored", "return act == 1 ? oracle_gelu_tanh(z) : oracle_silu(z);", "return oracle_silu(z);"),
     ("exact gate uses up weights", "g += (double)wg[j * d + i] * xb[i];", "g += (double)wu[j * d + i] * xb[i];"),
     ("down weight transposed", "(double)wd[m * F + sel[t]]", "(double)wd[(sel[t] * d + m) % (d * F)]"),
     ("one input too few kept", "for (int64_t t = 0; t < k_in; ++t)", "for (int64_t t = 0; t + 1 < k_in; ++t)"),

@@ -358,6 +358,74 @@ def test_zero_sparsity_is_dense_and_stage2_uses_dense_x(oracle):
     assert r1["k"] == 0 and not r1["y"].any()
 
 
+# ------------------------------------------------- activation and signals
+
+def _torch_gelu_tanh(z):
+    import torch
+    return torch.nn.functional.gelu(torch.as_tensor(np.asarray(z, dtype=np.float64)), approximate="tanh").numpy()
+
+
+def test_gelu_tanh_closed_forms_and_library(oracle):
+    # catches a wrong constant or a dropped cubic term
+    assert oracle.gelu_tanh(0.0) == 0.0
+    for z in (0.3, 1.0, 2.5, 7.0):
+        assert abs(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z) - z) < 1e-15 * max(1.0, z)
+    assert oracle.gelu_tanh(40.0) == 40.0 and oracle.gelu_tanh(-40.0) == 0.0
+    zs = np.linspace(-8, 8, 161)
+    np.testing.assert_allclose([oracle.gelu_tanh(z) for z in zs], _torch_gelu_tanh(zs), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_signals_match_numpy(oracle, act):
+    # the three proxy signals from the same g~, u~: |h~ u~|, |h~|, |u~|,
+    # h~ = act(g~), summed over the batch (catches a branch swapped or unsummed)
+    d, F, B = 128, 96, 2
+    wg, wu, _ = synth.make_weights(d, F, 0.05, "f32", seed=17)
+    x = synth.make_x(B, d, "f32", seed=17)
+    xh = oracle.input_select(x, 64)
+    qg, scg = oracle.quantize(wg, "int8_row")
+    qu, scu = oracle.quantize(wu, "int8_row")
+    g, u, _ = oracle.proxy(xh, qg, scg, qu, scu, "int8_row")
+    h = g * expit(g) if act == "silu" else _torch_gelu_tanh(g)
+    for sig, want in (("s", np.abs(h * u).sum(0)), ("h", np.abs(h).sum(0)), ("u", np.abs(u).sum(0))):
+        _, _, sc = oracle.proxy(xh, qg, scg, qu, scu, "int8_row", act, sig)
+        np.testing.assert_allclose(sc, want, rtol=1e-12, atol=1e-18)
+
+
+def test_exact_signal_is_the_exact_state(oracle):
+    # exact_s scores are |s| of the dense FFN; with keep 1 and weights on a
+    # lossless int8 grid the Prox proxy mask equals the exact-state mask
+    d, F = 64, 80
+    rng = np.random.default_rng(18)
+    wg = (rng.integers(-127, 128, (F, d)) * 2.0 ** -9).astype(np.float32)
+    wu = (rng.integers(-127, 128, (F, d)) * 2.0 ** -9).astype(np.float32)
+    wg[:, 0], wu[:, 0] = 127 * 2.0 ** -9, -127 * 2.0 ** -9
+    wd = synth.make_weights(d, F, 0.02, "f32", seed=18)[2]
+    x = synth.make_x(2, d, "f32", seed=18)
+    for act in ("silu", "gelu_tanh"):
+        sc = oracle.exact_scores(x, wg, wu, wd, act)
+        g, u = x.astype(np.float64) @ wg.T.astype(np.float64), x.astype(np.float64) @ wu.T.astype(np.float64)
+        h = g * expit(g) if act == "silu" else _torch_gelu_tanh(g)
+        np.testing.assert_allclose(sc, np.abs(h * u).sum(0), rtol=1e-12)
+        P = oracle.quantize(wg, "int8_row") + oracle.quantize(wu, "int8_row")
+        r_proxy = oracle.prox_forward(x, wg, wu, wd, P, 1.0, 0.6, "int8_row", act=act, signal="s")
+        r_exact = oracle.prox_forward(x, wg, wu, wd, P, 1.0, 0.6, "int8_row", act=act, signal="exact_s")
+        np.testing.assert_array_equal(r_proxy["sel"], r_exact["sel"])
+        np.testing.assert_allclose(r_proxy["score"], r_exact["score"], rtol=1e-12)
+
+
+def test_geglu_dense_matches_numpy(oracle):
+    d, F = 160, 128
+    wg, wu, wd = synth.make_weights(d, F, 0.05, "f32", seed=19)
+    x = synth.make_x(2, d, "f32", seed=19)
+    y, s = oracle.ffn_dense(x, wg, wu, wd, "gelu_tanh")
+    f = oracle.as_f64
+    g, u = f(x) @ f(wg).T, f(x) @ f(wu).T
+    s2 = _torch_gelu_tanh(g) * u
+    np.testing.assert_allclose(s, s2, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(y, s2 @ f(wd).T, rtol=1e-11, atol=1e-15)
+
+
 # ------------------------------------------------------------- FP8 E4M3
 # Facts of the OCP E4M3 format (not of the pages, which name FP8 only):
 # bias 7, subnormals down to 2^-9, largest finite 448, S.1111.111 = NaN.
