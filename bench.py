@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="mask recall of each selection signal against the exact-state mask, and its time")
     return ap.parse_args()
 
 
@@ -318,6 +320,31 @@ def main():
     print("dominant %s %.2f us/launch; dense %s us/layer" % (dom_kernel or dom, dom_us, dense_us),
           file=sys.stderr, flush=True)
 
+    # ---- selection-signal diagnostics: each signal's mask against the ideal
+    # (exact-state) mask of the same token, and the forward time with it
+    diagnostics = None
+    if args.diagnostics and 0 < k < F:
+        masks, times = {}, {}
+        for signal in ("exact_s", "s", "h", "u"):
+            sel_d = torch.empty(k, dtype=torch.int32, device=dev)
+            w, p = sets[0]
+            P.ffn_forward(x, w, p, keep, sp, out=out, sel_out=sel_d,
+                          workspace=ws, signal=signal)
+            torch.cuda.synchronize()
+            masks[signal] = set(sel_d.cpu().numpy().tolist())
+            n_s = max(R, args.steps // 8)
+            e0.record()
+            for i in range(n_s):
+                w, p = sets[i % R]
+                P.ffn_forward(x, w, p, keep, sp, out=out, workspace=ws,
+                              signal=signal)
+            e1.record()
+            torch.cuda.synchronize()
+            times[signal] = round(1000.0 * e0.elapsed_time(e1) / n_s, 3)
+        diagnostics = {sig: {"recall_vs_exact_state_mask": round(len(masks[sig] & masks["exact_s"]) / k, 4),
+                             "us_per_layer": times[sig]} for sig in masks}
+        print("diagnostics %s" % diagnostics, file=sys.stderr, flush=True)
+
     # ---- CPU oracle baseline (bounded sample on the host cores)
     cpu = None
     parity = None
@@ -387,6 +414,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if diagnostics is not None:
+        line["diagnostics"] = diagnostics
     print(json.dumps(line), flush=True)
 
     if args.copy_calibration:  # known-size copy for the memory-traffic counters

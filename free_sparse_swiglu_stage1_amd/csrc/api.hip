@@ -65,10 +65,27 @@ prox_status check_weights(const prox_weights *w)
     return PROX_OK;
 }
 
-S2Weights s2_weights(const prox_weights *w)
+// Forward options (prox_options, validated): gate activation and selection signal.
+struct Opts {
+    int act = PROX_ACT_SILU;
+    int signal = PROX_SIGNAL_S;
+};
+
+prox_status check_options(const prox_options *o, Opts *out)
+{
+    if (!o) return PROX_OK;
+    if (o->activation != PROX_ACT_SILU && o->activation != PROX_ACT_GELU_TANH) return PROX_ERR_UNSUPPORTED;
+    if (o->signal < PROX_SIGNAL_S || o->signal > PROX_SIGNAL_EXACT_S) return PROX_ERR_UNSUPPORTED;
+    out->act = o->activation;
+    out->signal = o->signal;
+    return PROX_OK;
+}
+
+S2Weights s2_weights(const prox_weights *w, int act)
 {
     const bool fp8 = w->wformat == PROX_W_FP8_E4M3;
-    return S2Weights{fp8 ? 1 : 0, w->w_gu, fp8 ? w->gu_scales : nullptr, w->w_down_t, fp8 ? w->down_scales : nullptr};
+    return S2Weights{fp8 ? 1 : 0, w->w_gu, fp8 ? w->gu_scales : nullptr, w->w_down_t,
+                     fp8 ? w->down_scales : nullptr, act};
 }
 
 prox_status check_proxy(const prox_proxy *p, const prox_weights *w)
@@ -191,7 +208,7 @@ hipError_t mark(hipEvent_t *ev, int i, hipStream_t st) { return ev ? hipEventRec
 // Stage 1 into `sel` (k entries), scores into `score`.
 prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const prox_proxy *p, int64_t k_in,
                        int64_t k, int32_t *sel, float *score, const Workspace &ws, hipStream_t st,
-                       hipEvent_t *ev = nullptr)
+                       hipEvent_t *ev = nullptr, const Opts &o = Opts())
 {
     const int64_t d = w->d_model, F = w->d_ff;
     const int dt = w->dtype == PROX_F32 ? 0 : 1;
@@ -199,7 +216,7 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
         TRY_HIP(mark(ev, 0, st));
         TRY_HIP(launch_stage1_fused(dt, p->mode == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
                                     (const uint8_t *)p->codes, (const float *)p->scales, ws.proxy_part, score, sel,
-                                    ws.counters, st));
+                                    ws.counters, o.act, o.signal, st));
         TRY_HIP(mark(ev, 1, st));
         return hip_status(mark(ev, 2, st));
     }
@@ -209,7 +226,7 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
                            kTicketWords, st));
     TRY_HIP(mark(ev, 1, st));
     TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes, (const float *)p->scales,
-                         ws.proxy_part, score, ws.counters, st));
+                         ws.proxy_part, score, ws.counters, o.act, o.signal, st));
     TRY_HIP(mark(ev, 2, st));
     if (k > 0) TRY_HIP(launch_topk(score, (int)F, (int)k, sel, st));
     return PROX_OK;
@@ -218,10 +235,11 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
 // Stage 2 on `sel` (nullptr = every channel).  Counters must be zero.
 prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const int32_t *sel, int64_t k,
                        const void *residual, void *out, int32_t *iota_out, const Workspace &ws, hipStream_t st,
-                       hipEvent_t *ev = nullptr)
+                       hipEvent_t *ev = nullptr, const Opts &o = Opts())
 {
     const int dt = w->dtype == PROX_F32 ? 0 : 1;
     const int64_t d = w->d_model;
+    const S2Weights sw = s2_weights(w, o.act);
     TRY_HIP(mark(ev, 3, st));
     if (k == 0) {
         TRY_HIP(launch_fill_out(dt, (int)B, (int)d, residual, out, st));
@@ -229,28 +247,56 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         return hip_status(mark(ev, 5, st));
     }
     if (B == 1) {  // one launch: the down projection starts while gate/up drains
-        TRY_HIP(launch_stage2_fused(dt, s2_weights(w), x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part,
-                                    residual, out, ws.counters, iota_out, st));
+        TRY_HIP(launch_stage2_fused(dt, sw, x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part, residual,
+                                    out, ws.counters, iota_out, st));
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
-    TRY_HIP(launch_gateup(dt, s2_weights(w), x, (int)B, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, iota_out, st));
+    TRY_HIP(launch_gateup(dt, sw, x, (int)B, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, iota_out, st));
     TRY_HIP(mark(ev, 4, st));
     const DownPlan dp = down_plan(d, k, B, w);
-    TRY_HIP(launch_down(dt, s2_weights(w), dp, ws.s_sp, (int)B, (int)k, sel, (int)d, (int)w->d_ff, ws.down_part,
-                        residual, out, ws.counters + kDownSliceBase, st));
+    TRY_HIP(launch_down(dt, sw, dp, ws.s_sp, (int)B, (int)k, sel, (int)d, (int)w->d_ff, ws.down_part, residual, out,
+                        ws.counters + kDownSliceBase, st));
     return hip_status(mark(ev, 5, st));
+}
+
+// The exact-state signal (no proxy, 0 < k < F): exact gate/up of every
+// channel with the dense x, score_j = sum_b |s_bj|, the top-k, then the down
+// projection on the selected channels' s values (gathered in rank order
+// into the proxy-partials area, unused on this path).
+prox_status run_exact_signal(const void *x, int64_t B, const prox_weights *w, int64_t k, int32_t *sel,
+                             const void *residual, void *out, const Workspace &ws, hipStream_t st, const Opts &o)
+{
+    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    const int64_t d = w->d_model, F = w->d_ff;
+    const S2Weights sw = s2_weights(w, o.act);
+    TRY_HIP(launch_gateup(dt, sw, x, (int)B, (int)d, (int)F, nullptr, (int)F, ws.s_sp, nullptr, st));
+    TRY_HIP(launch_score_from_s(ws.s_sp, (int)B, (int)F, ws.score, st));
+    TRY_HIP(launch_topk(ws.score, (int)F, (int)k, sel, st));
+    TRY_HIP(launch_gather_s(ws.s_sp, (int)B, (int)F, sel, (int)k, ws.proxy_part, st));
+    const DownPlan dp = down_plan(d, k, B, w);
+    return hip_status(launch_down(dt, sw, dp, ws.proxy_part, (int)B, (int)k, sel, (int)d, (int)F, ws.down_part,
+                                  residual, out, ws.counters + kDownSliceBase, st));
 }
 
 prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const prox_proxy *p, float keep,
                          float sp, const void *residual, void *out, int32_t *sel_out, void *workspace,
-                         size_t ws_bytes, hipStream_t st, hipEvent_t *ev = nullptr)
+                         size_t ws_bytes, hipStream_t st, hipEvent_t *ev = nullptr,
+                         const prox_options *opt = nullptr)
 {
-    prox_status s = check_weights(w);
+    Opts o;
+    prox_status s = check_options(opt, &o);
     if (s != PROX_OK) return s;
-    s = check_proxy(p, w);
+    if (o.signal == PROX_SIGNAL_EXACT_S && ev) return PROX_ERR_UNSUPPORTED;
+    s = check_weights(w);
     if (s != PROX_OK) return s;
-    s = check_batch(B, p->mode);
+    const bool exact = o.signal == PROX_SIGNAL_EXACT_S;  // no proxy is read
+    const int mode = exact ? (p ? (int)p->mode : (int)PROX_Q_INT8_ROW) : -1;
+    if (!exact || p) {
+        s = check_proxy(p, w);
+        if (s != PROX_OK) return s;
+    }
+    s = check_batch(B, exact ? mode : p->mode);
     if (s != PROX_OK) return s;
     if (bad_ptr(x) || bad_ptr(out) || bad_ptr_opt(sel_out) || bad_ptr_opt(residual) || bad_ptr(workspace))
         return PROX_ERR_INVALID_ARG;
@@ -258,19 +304,20 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     int64_t k_in, k;
     s = counts(w->d_model, w->d_ff, keep, sp, &k_in, &k);
     if (s != PROX_OK) return s;
-    const Workspace ws = layout(w->d_model, w->d_ff, B, p->mode, workspace);
+    const Workspace ws = layout(w->d_model, w->d_ff, B, exact ? mode : p->mode, workspace);
     if (ws_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
     const int64_t F = w->d_ff;
     if (k == 0 || k == F) {  // no Stage 1
         TRY_HIP(mark(ev, 0, st));
         TRY_HIP(mark(ev, 1, st));
         TRY_HIP(mark(ev, 2, st));
-        return run_stage2(x, B, w, nullptr, k, residual, out, k ? sel_out : nullptr, ws, st, ev);
+        return run_stage2(x, B, w, nullptr, k, residual, out, k ? sel_out : nullptr, ws, st, ev, o);
     }
     int32_t *sel = sel_out ? sel_out : ws.sel;
-    s = run_stage1(x, B, w, p, k_in, k, sel, ws.score, ws, st, ev);
+    if (exact) return run_exact_signal(x, B, w, k, sel, residual, out, ws, st, o);
+    s = run_stage1(x, B, w, p, k_in, k, sel, ws.score, ws, st, ev, o);
     if (s != PROX_OK) return s;
-    return run_stage2(x, B, w, sel, k, residual, out, nullptr, ws, st, ev);
+    return run_stage2(x, B, w, sel, k, residual, out, nullptr, ws, st, ev, o);
 }
 
 }  // namespace
@@ -391,6 +438,15 @@ prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_w
                         workspace_bytes, stream);
 }
 
+prox_status prox_ffn_forward_ex(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                                float input_keep, float ffn_sparsity, const prox_options *opt, const void *residual,
+                                void *out, int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream)
+{
+    return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, residual, out, sel_idx_out, workspace,
+                        workspace_bytes, stream, nullptr, opt);
+}
+
 prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
                                    float input_keep, float ffn_sparsity, void *out, int32_t *sel_idx_out,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events)
@@ -437,7 +493,17 @@ prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_id
 prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *w, const int32_t *sel_idx,
                               int64_t k, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    prox_status s = check_weights(w);
+    return prox_stage2_exact_ex(x, batch, w, sel_idx, k, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+prox_status prox_stage2_exact_ex(const void *x, int64_t batch, const prox_weights *w, const int32_t *sel_idx,
+                                 int64_t k, const prox_options *opt, void *out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
+{
+    Opts o;
+    prox_status s = check_options(opt, &o);
+    if (s != PROX_OK) return s;
+    s = check_weights(w);
     if (s != PROX_OK) return s;
     s = check_batch(batch, PROX_Q_INT8_ROW);
     if (s != PROX_OK) return s;
@@ -446,7 +512,7 @@ prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *
     if (x == out) return PROX_ERR_INVALID_ARG;
     const Workspace ws = layout(w->d_model, w->d_ff, batch, PROX_Q_INT8_ROW, workspace);
     if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
-    return run_stage2(x, batch, w, sel_idx, k, nullptr, out, nullptr, ws, stream);
+    return run_stage2(x, batch, w, sel_idx, k, nullptr, out, nullptr, ws, stream, nullptr, o);
 }
 
 prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d, prox_dtype dtype, float eps, void *out,

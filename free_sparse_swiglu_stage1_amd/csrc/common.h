@@ -195,6 +195,22 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // ---------------------------------------------------------------- silu
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// The gate activation h = act(g): 0 = silu (SwiGLU FFNs), 1 = gelu in its
+// tanh form (GeGLU FFNs, e.g. the Gemma family).
+__device__ __forceinline__ float gate_act(int act, float z)
+{
+    if (act == 1) return 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
+    return silu(z);
+}
+
+// A channel's salience term for the selection signal: 0 = |h u| (the
+// intermediate state), 1 = |h| (gate branch only), 2 = |u| (up branch only).
+__device__ __forceinline__ float salience(int signal, int act, float g, float u)
+{
+    const float h = gate_act(act, g);
+    return signal == 1 ? fabsf(h) : (signal == 2 ? fabsf(u) : fabsf(h * u));
+}
+
 // ---------------------------------------------------------- reductions
 // Cross-lane steps use DPP (row shifts within 16-lane rows, then row
 // broadcasts), which run at VALU speed; lane 63 ends with the full result.

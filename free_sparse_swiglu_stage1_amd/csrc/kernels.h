@@ -50,14 +50,21 @@ struct FusedPlan {
 
 FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
 bool fused_supported(int64_t B, int64_t d, int64_t F);
+// act: the gate activation (0 silu, 1 gelu tanh form); signal: the
+// selection signal (0 |act(g~) u~|, 1 |act(g~)|, 2 |u~|).
 hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
                                const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
-                               uint32_t *counters, hipStream_t st);
+                               uint32_t *counters, int act, int signal, hipStream_t st);
 
 hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
                           int n_counters, hipStream_t st);
 hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
-                        const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st);
+                        const float *scales, float *part, float *score, uint32_t *counters, int act, int signal,
+                        hipStream_t st);
+// The exact-state signal: score[j] = sum_b |s[b][j]| over s [B][F], and the
+// selected channels' values s_sel[b][r] = s[b][sel[r]].
+hipError_t launch_score_from_s(const float *s, int B, int F, float *score, hipStream_t st);
+hipError_t launch_gather_s(const float *s, int B, int F, const int32_t *sel, int k, float *s_sel, hipStream_t st);
 hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st);
 
 // Stage-2 weights as the kernels read them.  fmt 0: w_gu [F][2][d] and
@@ -70,6 +77,7 @@ struct S2Weights {
     const float *gu_scales;
     const void *w_down_t;
     const float *down_scales;
+    int act;  // gate activation: 0 silu, 1 gelu (tanh form)
 };
 
 // Stage 2 clamps every mask entry into [0, F): a malformed mask gives wrong

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
 // are added in LDS in a fixed order into this split's partial g~ / u~; the
 // last split to finish a channel block (atomic ticket) adds the partials in
 // split order, applies the per-channel scale (int8), and writes
-// score_j = sum_b |silu(g~_bj) u~_bj|.  Bitwise deterministic.
+// score_j = sum_b of the signal's salience term (|act(g~) u~| for Prox).
+// Bitwise deterministic.
 //
 // int4-g128: codes are biased nibbles (q + 8); per 128-input group each lane
 // accumulates sum x*(q+8) and sum x, and when the group changes adds
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
                                                     const uint8_t *__restrict__ codes,
                                                     const float *__restrict__ scales, int R, int S,
                                                     float *__restrict__ part, float *__restrict__ score,
-                                                    uint32_t *__restrict__ counters)
+                                                    uint32_t *__restrict__ counters, int act, int signal)
 {
     constexpr int NT = 256;
     constexpr int CPL = Codes<QBITS>::CPL;
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
         float sc = 0.0f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-            if (b < B) sc += fabsf(silu(g[b] * sg) * (u[b] * su));
+            if (b < B) sc += salience(signal, act, g[b] * sg, u[b] * su);
         score[j] = sc;
     }
 }
@@ -326,10 +327,12 @@ hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, floa
 }
 
 hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
-                        const float *scales, float *part, float *score, uint32_t *counters, hipStream_t st)
+                        const float *scales, float *part, float *score, uint32_t *counters, int act, int signal,
+                        hipStream_t st)
 {
     dim3 grid(pl.n_cblocks, pl.S);
-#define PX(Q, N) proxy_kernel<Q, N><<<grid, 256, 0, st>>>(xh, B, d, F, codes, scales, pl.R, pl.S, part, score, counters)
+#define PX(Q, N) \
+    proxy_kernel<Q, N><<<grid, 256, 0, st>>>(xh, B, d, F, codes, scales, pl.R, pl.S, part, score, counters, act, signal)
     if (pl.qbits == 8) {
         if (pl.nb == 1) PX(8, 1);
         else if (pl.nb == 4) PX(8, 4);

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
                                                            const float *__restrict__ scales, int R, int S,
                                                            int n_cblocks, float *__restrict__ part,
                                                            float *__restrict__ score, int32_t *__restrict__ sel,
-                                                           uint32_t *__restrict__ counters)
+                                                           uint32_t *__restrict__ counters, int act, int signal)
 {
     using Q = Fused<QBITS>;
     constexpr int CPL = Q::CPL;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
                     g *= scales[j + q];
                     u *= scales[F + j + q];
                 }
-                sc[q] = fabsf(silu(g) * u);
+                sc[q] = salience(signal, act, g, u);
             }
             store_agent2(&score[j], sc[0], sc[1]);
         }
@@ -329,7 +329,7 @@ bool fused_supported(int64_t B, int64_t d, int64_t F) { return B == 1 && d <= kF
 
 hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
                                const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
-                               uint32_t *counters, hipStream_t st)
+                               uint32_t *counters, int act, int signal, hipStream_t st)
 {
     if (!fused_supported(1, d, F)) return hipErrorInvalidValue;
     const FusedPlan pl = fused_plan(qbits, d, F);
@@ -339,7 +339,7 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
 #define L1(T, Q, KXV, KFV)                                                                               \
     stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k, codes, scales, \
                                                              pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
-                                                             counters)
+                                                             counters, act, signal)
 #define L2(T, Q)                                       \
     do {                                               \
         if (kx <= 2 && kf <= 16) L1(T, Q, 2, 16);      \

@@ -159,7 +159,7 @@ template <typename T, typename TW, int NB, bool COHERENT>
 __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int d, int F,
                                              const TW *__restrict__ w_gu, const float *__restrict__ gsc,
                                              const int32_t *__restrict__ sel, int k, float *__restrict__ s_sp,
-                                             int32_t *__restrict__ iota_out, float *xs, int blk)
+                                             int32_t *__restrict__ iota_out, float *xs, int blk, int act)
 {
     constexpr int V = WRows<TW>::GV;     // elements per 16-byte load
     constexpr int UNR = WRows<TW>::UNR;  // 16-byte vectors per lane per pass (two rows: 2*UNR loads)
@@ -233,9 +233,9 @@ __device__ __forceinline__ void gateup_block(const T *__restrict__ x, int B, int
         const float u = us * wave_sum(au[b]);
         if (live && lane == 0 && b < B) {
             if (COHERENT)
-                store_agent(&s_sp[(int64_t)b * k + r], silu(g) * u);
+                store_agent(&s_sp[(int64_t)b * k + r], gate_act(act, g) * u);
             else
-                s_sp[(int64_t)b * k + r] = silu(g) * u;
+                s_sp[(int64_t)b * k + r] = gate_act(act, g) * u;
         }
     }
 }
@@ -244,10 +244,10 @@ template <typename T, typename TW, int NB>
 __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, int B, int d, int F,
                                                      const TW *__restrict__ w_gu, const float *__restrict__ gsc,
                                                      const int32_t *__restrict__ sel, int k, float *__restrict__ s_sp,
-                                                     int32_t *__restrict__ iota_out)
+                                                     int32_t *__restrict__ iota_out, int act)
 {
     extern __shared__ float xs[];  // [NB][d]
-    gateup_block<T, TW, NB, false>(x, B, d, F, w_gu, gsc, sel, k, s_sp, iota_out, xs, blockIdx.x);
+    gateup_block<T, TW, NB, false>(x, B, d, F, w_gu, gsc, sel, k, s_sp, iota_out, xs, blockIdx.x, act);
 }
 
 // ------------------------------------------------------------------------
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
     const T *__restrict__ x, int d, int F, const TW *__restrict__ w_gu, const float *__restrict__ gsc,
     const TW *__restrict__ wdt, const float *__restrict__ dsc, const int32_t *__restrict__ sel, int k, int n_gu,
     int n_slices, int S, float *__restrict__ s_sp, float *__restrict__ part, const T *residual, T *out,
-    uint32_t *__restrict__ counters, int32_t *__restrict__ iota_out)
+    uint32_t *__restrict__ counters, int32_t *__restrict__ iota_out, int act)
 {
     constexpr int V = WRows<TW>::DV;
     constexpr int COLS = 64 * V;
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
 
     if ((int)blockIdx.x < n_gu) {
-        gateup_block<T, TW, 1, true>(x, 1, d, F, w_gu, gsc, sel, k, s_sp, iota_out, dyn, blockIdx.x);
+        gateup_block<T, TW, 1, true>(x, 1, d, F, w_gu, gsc, sel, k, s_sp, iota_out, dyn, blockIdx.x, act);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's s stores have completed
         __syncthreads();
         if (tid == 0)
@@ -562,10 +562,10 @@ static hipError_t gateup_t(const void *x, int B, int d, int F, const S2Weights &
         int32_t *io = (b0 == 0) ? iota_out : nullptr;
         if (nb == 1)
             gateup_kernel<T, TW, 1><<<blocks, 256, xpad_row<gu_xpad<TW, 1>()>(d) * sizeof(float), st>>>(
-                xp, 1, d, F, wgu, w.gu_scales, sel, k, sp, io);
+                xp, 1, d, F, wgu, w.gu_scales, sel, k, sp, io, w.act);
         else
             gateup_kernel<T, TW, 4><<<blocks, 256, 4 * d * sizeof(float), st>>>(xp, nb, d, F, wgu, w.gu_scales,
-                                                                                sel, k, sp, io);
+                                                                                sel, k, sp, io, w.act);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -634,7 +634,7 @@ static hipError_t stage2_fused_t(const void *x, int d, int F, const S2Weights &w
     const size_t lds = sizeof(float) * (size_t)max(xpad_row<gu_xpad<TW, 1>()>(d), kS2Waves * 64 * V);
     stage2_fused_kernel<T, TW><<<grid, 64 * kS2Waves, lds, st>>>(
         (const T *)x, d, F, (const TW *)w.w_gu, w.gu_scales, (const TW *)w.w_down_t, w.down_scales, sel, k, n_gu,
-        n_slices, S, s_sp, part, (const T *)residual, (T *)out, counters, iota_out);
+        n_slices, S, s_sp, part, (const T *)residual, (T *)out, counters, iota_out, w.act);
     return hipGetLastError();
 }
 
@@ -652,6 +652,42 @@ hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int
                                                      iota_out, st)
                       : stage2_fused_t<uint16_t, uint16_t>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
                                                            iota_out, st);
+}
+
+// ------------------------------------------------------------------------
+// The exact-state signal (no proxy): score_j = sum_b |s_bj| from the dense
+// exact gate/up of every channel, and the gather of the selected channels'
+// s values in rank order for the down projection.
+// ------------------------------------------------------------------------
+__global__ void score_from_s_kernel(const float *__restrict__ s, int B, int F, float *__restrict__ score)
+{
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= F) return;
+    float sc = 0.0f;
+    for (int b = 0; b < B; ++b) sc += fabsf(s[(int64_t)b * F + j]);
+    score[j] = sc;
+}
+
+__global__ void gather_s_kernel(const float *__restrict__ s, int B, int F, const int32_t *__restrict__ sel, int k,
+                                float *__restrict__ s_sel)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= k) return;
+    const int j = (int)min((uint32_t)sel[r], (uint32_t)(F - 1));
+    for (int b = 0; b < B; ++b) s_sel[(int64_t)b * k + r] = s[(int64_t)b * F + j];
+}
+
+hipError_t launch_score_from_s(const float *s, int B, int F, float *score, hipStream_t st)
+{
+    score_from_s_kernel<<<(F + 255) / 256, 256, 0, st>>>(s, B, F, score);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_s(const float *s, int B, int F, const int32_t *sel, int k, float *s_sel, hipStream_t st)
+{
+    if (k <= 0) return hipSuccess;
+    gather_s_kernel<<<(k + 255) / 256, 256, 0, st>>>(s, B, F, sel, k, s_sel);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st)

@@ -20,6 +20,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 Q_INT8_ROW, Q_INT4_G128 = 0, 1
 W_NATIVE, W_FP8_E4M3 = 0, 1
+ACTIVATIONS = {"silu": 0, "gelu_tanh": 1}
+SIGNALS = {"s": 0, "h": 1, "u": 2, "exact_s": 3}
 MODES = {"int8_row": Q_INT8_ROW, "int4_g128": Q_INT4_G128}
 
 SYMBOLS = (
@@ -27,6 +29,7 @@ SYMBOLS = (
     "prox_proxy_sizes",
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
+    "prox_ffn_forward_ex", "prox_stage2_exact_ex",
 )
 
 
@@ -41,6 +44,10 @@ class _CWeights(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64), ("dtype", ctypes.c_int),
                 ("w_gu", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p), ("wformat", ctypes.c_int),
                 ("gu_scales", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
+
+
+class _COptions(ctypes.Structure):
+    _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int)]
 
 
 class _CProxy(ctypes.Structure):
@@ -65,6 +72,7 @@ def load_library(path: str = LIB_PATH):
     PI = ctypes.POINTER(ctypes.c_int64)
     PW = ctypes.POINTER(_CWeights)
     PP = ctypes.POINTER(_CProxy)
+    PO = ctypes.POINTER(_COptions)
     sig = {
         "prox_status_string": ([I32], ctypes.c_char_p),
         "prox_version": ([], ctypes.c_char_p),
@@ -83,6 +91,8 @@ def load_library(path: str = LIB_PATH):
         "prox_stage2_exact": ([P, I64, PW, P, I64, P, P, ctypes.c_size_t, P], I32),
         "prox_rmsnorm": ([P, I64, I64, I32, F, P, P], I32),
         "prox_chain_forward": ([P, I64, PW, PP, I64, F, F, F, P, ctypes.c_size_t, P], I32),
+        "prox_ffn_forward_ex": ([P, I64, PW, PP, F, F, PO, P, P, P, P, ctypes.c_size_t, P], I32),
+        "prox_stage2_exact_ex": ([P, I64, PW, P, I64, PO, P, P, ctypes.c_size_t, P], I32),
     }
     for name in SYMBOLS:
         fn = getattr(lib, name)
@@ -249,16 +259,28 @@ def _mode_name(p: Proxy) -> str:
 
 def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sparsity: float,
                 out: torch.Tensor = None, sel_out: torch.Tensor = None, workspace: torch.Tensor = None,
-                residual: torch.Tensor = None) -> torch.Tensor:
-    """The Prox FFN forward on x[B][d]; returns out[B][d] (out = residual + y if residual is given)."""
+                residual: torch.Tensor = None, activation: str = "silu", signal: str = "s") -> torch.Tensor:
+    """The Prox FFN forward on x[B][d]; returns out[B][d] (out = residual + y if residual is given).
+
+    activation: "silu" (SwiGLU) or "gelu_tanh" (GeGLU); signal: the channel
+    selection signal, "s" (Prox), "h" / "u" (one proxy branch) or "exact_s"
+    (the exact state, no proxy; p may then be None)."""
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
-        workspace = alloc_workspace(w.d_model, w.d_ff, B, _mode_name(p), x.device)
-    cw, cp = w.c(), p.c()
+        workspace = alloc_workspace(w.d_model, w.d_ff, B, _mode_name(p) if p is not None else "int8_row", x.device)
+    cw = w.c()
+    if activation != "silu" or signal != "s":
+        opt = _COptions(ACTIVATIONS[activation], SIGNALS[signal])
+        st = lib.prox_ffn_forward_ex(_ptr(x), B, ctypes.byref(cw), ctypes.byref(p.c()) if p is not None else None,
+                                     input_keep, ffn_sparsity, ctypes.byref(opt), _ptr(residual), _ptr(out),
+                                     _ptr(sel_out), _ptr(workspace), workspace.numel(), _stream(x.device))
+        _check(st, "prox_ffn_forward_ex")
+        return out
+    cp = p.c()
     if residual is None:
         st = lib.prox_ffn_forward(_ptr(x), B, ctypes.byref(cw), ctypes.byref(cp), input_keep, ffn_sparsity,
                                   _ptr(out), _ptr(sel_out), _ptr(workspace), workspace.numel(), _stream(x.device))
@@ -322,7 +344,7 @@ def topk(scores: torch.Tensor, k: int) -> torch.Tensor:
 
 
 def stage2_exact(x: torch.Tensor, w: Weights, sel: torch.Tensor, out: torch.Tensor = None,
-                 workspace: torch.Tensor = None) -> torch.Tensor:
+                 workspace: torch.Tensor = None, activation: str = "silu") -> torch.Tensor:
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
@@ -332,6 +354,12 @@ def stage2_exact(x: torch.Tensor, w: Weights, sel: torch.Tensor, out: torch.Tens
         workspace = alloc_workspace(w.d_model, w.d_ff, B, "int8_row", x.device)
     cw = w.c()
     sel = sel.to(torch.int32).contiguous() if sel.numel() else sel
+    if activation != "silu":
+        opt = _COptions(ACTIVATIONS[activation], 0)
+        _check(lib.prox_stage2_exact_ex(_ptr(x), B, ctypes.byref(cw), _ptr(sel) if sel.numel() else None,
+                                        sel.numel(), ctypes.byref(opt), _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(x.device)), "prox_stage2_exact_ex")
+        return out
     _check(lib.prox_stage2_exact(_ptr(x), B, ctypes.byref(cw), _ptr(sel) if sel.numel() else None, sel.numel(),
                                  _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device)),
            "prox_stage2_exact")

@@ -198,6 +198,39 @@ prox_status prox_ffn_forward_residual(const void *x, int64_t batch, const prox_w
                                       const void *residual, void *out, int32_t *sel_idx_out,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gate activation h = act(g).  SILU: silu(z) = z / (1 + exp(-z)) (SwiGLU).
+ * GELU_TANH: z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) (GeGLU FFNs, e.g.
+ * the Gemma family the pages evaluate, technical summary, Key
+ * Contributions).  Used by the salience and by Stage 2, s = act(g) * u. */
+typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
+
+/* Channel-selection signal (technical summary, Problem Statement: the exact
+ * intermediate state s = u (.) h is the ideal signal, prior methods use one
+ * branch, h or u):
+ *   S       |h~ u~| of the proxy (Prox; the default);
+ *   H       |h~|, the proxy gate branch alone;
+ *   U       |u~|, the proxy up branch alone;
+ *   EXACT_S |h u| of the exact state: exact gate/up of every channel with the
+ *           dense x (dense Stage-2 gate/up cost), no proxy -- the ideal mask,
+ *           a diagnostic.
+ * Each is summed over the batch before the top-k. */
+typedef enum { PROX_SIGNAL_S = 0, PROX_SIGNAL_H = 1, PROX_SIGNAL_U = 2, PROX_SIGNAL_EXACT_S = 3 } prox_signal;
+
+typedef struct {
+    prox_activation activation;
+    prox_signal signal;
+} prox_options;
+
+/* prox_ffn_forward with options (opt NULL = SILU and S, i.e. prox_ffn_forward)
+ * and an optional residual (nullable; as prox_ffn_forward_residual).  With
+ * PROX_SIGNAL_EXACT_S, p may be NULL (no proxy is read); the workspace is then
+ * sized for PROX_Q_INT8_ROW.  Unknown options: PROX_ERR_UNSUPPORTED. */
+prox_status prox_ffn_forward_ex(const void *x, int64_t batch, const prox_weights *w,
+                                const prox_proxy *p, float input_keep, float ffn_sparsity,
+                                const prox_options *opt, const void *residual, void *out,
+                                int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* prox_ffn_forward with timing marks: events[0..5] (host array of six
  * hipEvent_t the caller created) are recorded on the stream before the input
  * selection, the proxy GEMV, the top-k, the gate/up GEMV and the down
@@ -237,6 +270,12 @@ prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_id
 prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *w,
                               const int32_t *sel_idx, int64_t k, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* prox_stage2_exact with options (only the activation applies; opt NULL =
+ * SILU). */
+prox_status prox_stage2_exact_ex(const void *x, int64_t batch, const prox_weights *w,
+                                 const int32_t *sel_idx, int64_t k, const prox_options *opt, void *out,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* RMSNorm with unit gain: out = h / sqrt(mean(h^2) + eps), fp32 math, rounded
  * to the dtype.  h, out [B][d] device (may alias). */

@@ -163,6 +163,15 @@ def test_other_entry_points_reject(lib):
     assert lib.prox_pack_weights(v(FAKE), v(FAKE), v(0), 4096, 14336, B.BF16, v(FAKE), v(FAKE),
                                  None) == B.ERR_INVALID_ARG
     assert lib.prox_quantize_proxy(ctypes.byref(w), 3, v(FAKE), v(FAKE), None) == B.ERR_UNSUPPORTED
+    for act, sig in ((7, 0), (0, 9), (-1, 0)):  # unknown options are refused before any launch
+        opt = B._COptions(act, sig)
+        assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
+                                       v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
+        assert lib.prox_stage2_exact_ex(v(FAKE), 1, ctypes.byref(w), v(FAKE + 64), 5, ctypes.byref(opt),
+                                        v(FAKE + 128), v(FAKE + 256), 1 << 40, None) == B.ERR_UNSUPPORTED
+    opt = B._COptions(0, 1)  # a proxy signal needs the proxy
+    assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), None, 0.5, 0.7, ctypes.byref(opt), None,
+                                   v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_INVALID_ARG
     f8 = (v(FAKE), v(FAKE + 64), v(FAKE + 128), v(FAKE + 192))
     assert lib.prox_pack_weights_fp8(v(FAKE), v(FAKE), v(FAKE), 4104, 14336, B.BF16, *f8, None) == B.ERR_UNSUPPORTED
     assert lib.prox_pack_weights_fp8(v(FAKE), v(FAKE), v(FAKE), 4096, 14336, 5, *f8, None) == B.ERR_UNSUPPORTED
