@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="fit the sparsity-allocation cost model from measured stage times and test its plans")
     ap.add_argument("--diagnostics", action="store_true",
                     help="mask recall of each selection signal against the exact-state mask, and its time")
     return ap.parse_args()
@@ -320,6 +322,57 @@ def main():
     print("dominant %s %.2f us/launch; dense %s us/layer" % (dom_kernel or dom, dom_us, dense_us),
           file=sys.stderr, flush=True)
 
+    # ---- sparsity-allocation cost model: stage times measured live at several
+    # fractions, a straight line fitted to each, the dense layer as the unit;
+    # then the library's allocation for a few targets, timed end to end
+    calibration = None
+    if args.calibrate:
+        keeps = [0.3, 0.5, 0.7, 1.0]
+        t1 = []
+        for kp in keeps:
+            def s1k(i, kp=kp):
+                w, p = sets[i % R]
+                P.stage1_select(x, w, p, kp, sp, workspace=ws, sel_out=sel_buf)
+            t1.append(live_us(s1k))
+        kappas = [0.1, 0.3, 0.5, 0.7, 0.9]
+        t2 = []
+        rng = np.random.default_rng(7)
+        for kap in kappas:
+            kk = int(round(kap * F))
+            selk = torch.from_numpy(np.sort(rng.choice(F, kk, replace=False)).astype(np.int32)).to(dev)
+            def s2k(i, selk=selk):
+                w, _ = sets[i % R]
+                P.stage2_exact(x, w, selk, out=out, workspace=ws)
+            t2.append(live_us(s2k))
+        b1, a1 = np.polyfit(keeps, t1, 1)
+        b2, a2 = np.polyfit(kappas, t2, 1)
+        def dense_launch(i):
+            w, p = sets[i % R]
+            P.ffn_forward(x, w, p, keep, 0.0, out=out, workspace=ws)
+        t_dense = live_us(dense_launch)
+        model = (max(a1, 0.0), max(b1, 0.0), max(a2, 0.0), b2, t_dense)
+        plans = {}
+        for target in (0.3, 0.4, 0.5):
+            plan = P.allocate_sparsity(model, target)
+            if plan is None:
+                plans[str(target)] = None
+                continue
+            kp, spp = plan
+            def fwd(i, kp=kp, spp=spp):
+                w, p = sets[i % R]
+                P.ffn_forward(x, w, p, kp, spp, out=out, workspace=ws)
+            t_plan = live_us(fwd)
+            plans[str(target)] = {"input_keep": round(kp, 4), "ffn_sparsity": round(spp, 4),
+                                  "predicted_us": round((1.0 - target) * t_dense, 3), "measured_us": round(t_plan, 3),
+                                  "measured_effective_sparsity": round(1.0 - t_plan / t_dense, 4)}
+        calibration = {"stage1_us": dict(zip(map(str, keeps), [round(v, 3) for v in t1])),
+                       "stage2_us": dict(zip(map(str, kappas), [round(v, 3) for v in t2])),
+                       "dense_us": round(t_dense, 3),
+                       "model": dict(zip(("stage1_fixed_us", "stage1_per_keep_us", "stage2_fixed_us",
+                                          "stage2_per_kept_us", "dense_us"), [round(v, 4) for v in model])),
+                       "plans": plans}
+        print("calibration %s" % json.dumps(calibration), file=sys.stderr, flush=True)
+
     # ---- selection-signal diagnostics: each signal's mask against the ideal
     # (exact-state) mask of the same token, and the forward time with it
     diagnostics = None
@@ -416,6 +469,8 @@ def main():
     }
     if diagnostics is not None:
         line["diagnostics"] = diagnostics
+    if calibration is not None:
+        line["calibration"] = calibration
     print(json.dumps(line), flush=True)
 
     if args.copy_calibration:  # known-size copy for the memory-traffic counters

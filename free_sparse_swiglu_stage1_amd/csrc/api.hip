@@ -346,6 +346,45 @@ prox_status prox_counts(int64_t d, int64_t F, float keep, float sp, int64_t *k_i
     return counts(d, F, keep, sp, k_in, k);
 }
 
+prox_status prox_effective_sparsity(const prox_cost_model *m, double keep, double sp, double *effective)
+{
+    if (!m || !effective || !(m->dense_us > 0.0)) return PROX_ERR_INVALID_ARG;
+    if (!(keep >= 0.0 && keep <= 1.0) || !(sp >= 0.0 && sp <= 1.0)) return PROX_ERR_INVALID_ARG;
+    const double t = m->stage1_fixed_us + m->stage1_per_keep_us * keep + m->stage2_fixed_us +
+                     m->stage2_per_kept_us * (1.0 - sp);
+    *effective = 1.0 - t / m->dense_us;
+    return PROX_OK;
+}
+
+prox_status prox_allocate_sparsity(const prox_cost_model *m, double target, double anchor, double min_keep,
+                                   double *keep_out, double *sp_out)
+{
+    if (!m || !keep_out || !sp_out) return PROX_ERR_INVALID_ARG;
+    const double a1 = m->stage1_fixed_us, b1 = m->stage1_per_keep_us;
+    const double a2 = m->stage2_fixed_us, b2 = m->stage2_per_kept_us;
+    if (!(a1 >= 0.0 && b1 >= 0.0 && a2 >= 0.0 && b2 > 0.0 && m->dense_us > 0.0)) return PROX_ERR_INVALID_ARG;
+    if (!(anchor >= 0.0 && anchor <= 1.0) || !(min_keep > 0.0 && min_keep <= 1.0) || !(target < 1.0))
+        return PROX_ERR_INVALID_ARG;
+    const double budget = (1.0 - target) * m->dense_us;  // the time the layer may take
+    double keep = 1.0;
+    if (b1 > 0.0) {
+        // the anchor held: Stage 1 gets what Stage 2 at the anchor leaves
+        keep = (budget - a1 - a2 - b2 * (1.0 - anchor)) / b1;
+        if (keep >= min_keep && keep <= 1.0) {
+            *keep_out = keep;
+            *sp_out = anchor;
+            return PROX_OK;
+        }
+        keep = keep > 1.0 ? 1.0 : min_keep;
+    }
+    // keep at its bound: Stage 2 gets the rest
+    const double kappa = (budget - a1 - b1 * keep - a2) / b2;
+    if (kappa < 0.0) return PROX_ERR_UNSUPPORTED;
+    *keep_out = keep;
+    *sp_out = 1.0 - (kappa < 1.0 ? kappa : 1.0);
+    return PROX_OK;
+}
+
 prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *w_down, int64_t d, int64_t F,
                               prox_dtype dtype, void *w_gu_out, void *w_down_t_out, hipStream_t stream)
 {

@@ -29,7 +29,7 @@ SYMBOLS = (
     "prox_proxy_sizes",
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
-    "prox_ffn_forward_ex", "prox_stage2_exact_ex",
+    "prox_ffn_forward_ex", "prox_stage2_exact_ex", "prox_effective_sparsity", "prox_allocate_sparsity",
 )
 
 
@@ -48,6 +48,12 @@ class _CWeights(ctypes.Structure):
 
 class _COptions(ctypes.Structure):
     _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int)]
+
+
+class _CCostModel(ctypes.Structure):
+    _fields_ = [("stage1_fixed_us", ctypes.c_double), ("stage1_per_keep_us", ctypes.c_double),
+                ("stage2_fixed_us", ctypes.c_double), ("stage2_per_kept_us", ctypes.c_double),
+                ("dense_us", ctypes.c_double)]
 
 
 class _CProxy(ctypes.Structure):
@@ -73,6 +79,9 @@ def load_library(path: str = LIB_PATH):
     PW = ctypes.POINTER(_CWeights)
     PP = ctypes.POINTER(_CProxy)
     PO = ctypes.POINTER(_COptions)
+    PM = ctypes.POINTER(_CCostModel)
+    D = ctypes.c_double
+    PD = ctypes.POINTER(ctypes.c_double)
     sig = {
         "prox_status_string": ([I32], ctypes.c_char_p),
         "prox_version": ([], ctypes.c_char_p),
@@ -93,6 +102,8 @@ def load_library(path: str = LIB_PATH):
         "prox_chain_forward": ([P, I64, PW, PP, I64, F, F, F, P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward_ex": ([P, I64, PW, PP, F, F, PO, P, P, P, P, ctypes.c_size_t, P], I32),
         "prox_stage2_exact_ex": ([P, I64, PW, P, I64, PO, P, P, ctypes.c_size_t, P], I32),
+        "prox_effective_sparsity": ([PM, D, D, PD], I32),
+        "prox_allocate_sparsity": ([PM, D, D, D, PD, PD], I32),
     }
     for name in SYMBOLS:
         fn = getattr(lib, name)
@@ -213,6 +224,27 @@ def pack_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Ten
                                      _ptr(w_gu), _ptr(gsc), _ptr(w_dt), _ptr(dsc), _stream(dev)),
            "prox_pack_weights_fp8")
     return Weights(w_gu, w_dt, d, F, act_dtype=w_gate.dtype, gu_scales=gsc, down_scales=dsc)
+
+
+def effective_sparsity(model, input_keep: float, ffn_sparsity: float) -> float:
+    """model = (stage1_fixed_us, stage1_per_keep_us, stage2_fixed_us, stage2_per_kept_us, dense_us)."""
+    lib = load_library()
+    e = ctypes.c_double()
+    _check(lib.prox_effective_sparsity(ctypes.byref(_CCostModel(*model)), input_keep, ffn_sparsity, ctypes.byref(e)),
+           "prox_effective_sparsity")
+    return e.value
+
+
+def allocate_sparsity(model, target_effective: float, s2_anchor: float = 0.7, min_keep: float = 0.3):
+    """(input_keep, ffn_sparsity) for a target effective sparsity (see include/prox.h); None if unreachable."""
+    lib = load_library()
+    k, s = ctypes.c_double(), ctypes.c_double()
+    st = lib.prox_allocate_sparsity(ctypes.byref(_CCostModel(*model)), target_effective, s2_anchor, min_keep,
+                                    ctypes.byref(k), ctypes.byref(s))
+    if st == ERR_UNSUPPORTED:
+        return None
+    _check(st, "prox_allocate_sparsity")
+    return k.value, s.value
 
 
 def proxy_sizes(d: int, F: int, mode: str):

@@ -112,6 +112,42 @@ typedef struct {
     const void *scales; /* device */
 } prox_proxy;
 
+/* Sparsity allocation (technical summary, Sparsity Allocation: Stage-2
+ * sparsity anchored near 70%, Stage 1 keeping at least 30% of the inputs, a
+ * cost model choosing both for a target effective sparsity at the least
+ * normalized cost, counting the proxy's overhead).  The pages give no
+ * formula; the reading taken:
+ *   t1(keep)  = stage1_fixed_us + stage1_per_keep_us * keep   (Stage 1)
+ *   t2(kappa) = stage2_fixed_us + stage2_per_kept_us * kappa  (Stage 2,
+ *               kappa = 1 - ffn_sparsity, the kept channel fraction)
+ * fitted from measured times on the device (bench.py --calibrate), and
+ *   effective sparsity = 1 - (t1(keep) + t2(kappa)) / dense_us.
+ * All host-only. */
+typedef struct {
+    double stage1_fixed_us, stage1_per_keep_us;
+    double stage2_fixed_us, stage2_per_kept_us;
+    double dense_us;
+} prox_cost_model;
+
+/* Effective sparsity of (input_keep, ffn_sparsity) under the model.
+ * Requires dense_us > 0, keep and sparsity in [0,1]. */
+prox_status prox_effective_sparsity(const prox_cost_model *m, double input_keep, double ffn_sparsity,
+                                    double *effective);
+
+/* (input_keep, ffn_sparsity) for a target effective sparsity, the target
+ * read as a time budget (1 - target) * dense_us split between the stages:
+ *   1. hold ffn_sparsity at s2_anchor and solve for input_keep;
+ *   2. if that keep is above 1, keep every input and spend the rest on more
+ *      exact channels (ffn_sparsity below the anchor, not below 0);
+ *   3. if it is below min_keep, keep min_keep and raise ffn_sparsity.
+ * A keep-independent Stage 1 (stage1_per_keep_us == 0) keeps every input.
+ * Returns PROX_ERR_UNSUPPORTED when even ffn_sparsity = 1 at min_keep misses
+ * the target; PROX_ERR_INVALID_ARG for a negative cost, dense_us <= 0,
+ * stage2_per_kept_us <= 0, s2_anchor outside [0,1], min_keep outside (0,1]
+ * or a target not below 1. */
+prox_status prox_allocate_sparsity(const prox_cost_model *m, double target_effective, double s2_anchor,
+                                   double min_keep, double *input_keep_out, double *ffn_sparsity_out);
+
 /* Human-readable name of a status code (static string). */
 const char *prox_status_string(int status);
 

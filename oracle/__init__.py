@@ -322,6 +322,42 @@ def prox_forward(x, wg, wu, wd, proxy_q, input_keep: float, ffn_sparsity: float,
     return dict(k_in=k_in, k=k, xhat=xhat, g_proxy=gt, u_proxy=ut, score=score, sel=sel, T=T, y=y, s=s)
 
 
+# ------------------------------------------------- sparsity allocation
+# The pages (technical summary, Sparsity Allocation): Stage 2 sparsity is
+# anchored near 70%; Stage 1 keeps at least 30% of the inputs; a cost model
+# picks both to meet a target effective sparsity at the least normalized
+# cost, counting the proxy's overhead.  Reading: the normalized cost of a
+# layer is (t1(keep) + t2(kappa)) / t_dense with t1, t2 the measured Stage-1
+# and Stage-2 times, each linear in its fraction (keep = kept inputs, kappa =
+# 1 - sparsity = kept channels); the effective sparsity is 1 - that cost.  A
+# target is a cost budget; it is split by holding Stage-2 sparsity at the
+# anchor and solving for keep, then -- when keep would leave [min_keep, 1] --
+# holding keep at that bound and solving for the sparsity instead.
+
+def effective_sparsity(model, keep: float, sparsity: float) -> float:
+    """model = (a1, b1, a2, b2, dense): t1 = a1 + b1 keep, t2 = a2 + b2 (1 - sparsity)."""
+    a1, b1, a2, b2, dense = model
+    return 1.0 - (a1 + b1 * keep + a2 + b2 * (1.0 - sparsity)) / dense
+
+
+def allocate_sparsity(model, target: float, anchor: float = 0.7, min_keep: float = 0.3):
+    """(keep, sparsity) meeting the target effective sparsity, or None when even
+    dropping every channel at the least keep misses it."""
+    a1, b1, a2, b2, dense = model
+    budget = (1.0 - target) * dense          # time the layer may take
+    if b1 > 0:  # hold the anchor, solve for keep
+        keep = (budget - a1 - a2 - b2 * (1.0 - anchor)) / b1
+        if min_keep <= keep <= 1.0:
+            return keep, anchor
+        keep = 1.0 if keep > 1.0 else min_keep
+    else:       # keep costs nothing: keep every input
+        keep = 1.0
+    kappa = (budget - a1 - b1 * keep - a2) / b2
+    if kappa < 0.0:
+        return None
+    return keep, 1.0 - min(kappa, 1.0)
+
+
 def ambiguous_set(score: np.ndarray, T: float, rel: float = 1e-4) -> np.ndarray:
     """Channels whose score lies within ``rel`` (relative) of the k-th score."""
     score = np.asarray(score, dtype=np.float64)
