@@ -16,7 +16,8 @@ constexpr int kMaxBatch = 16;
 constexpr int kMaxBatchInt4 = 4;
 // The workspace starts with counters that must be zero between calls:
 // [0,511) proxy channel blocks, 511 the single-token Stage 1's score ticket,
-// [512,576) down slices, 1023 a wait-timeout flag, then from 4096 the
+// [512,1023) down slices, 1023 a wait-timeout flag, [1024,1535) the
+// single-token Stage 2's finished slice tails, then from 4096 the
 // single-token Stage 2's per-split lines (64 pages of 4 KB).  Each is reset
 // by the last workgroup to use it.
 constexpr int kCounters = kS2SyncBase + kS2SyncWords;

@@ -88,13 +88,15 @@ hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const 
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
 // Stage 2 for one token in one launch (stage2.hip).  Counter slots:
-// [kDownSliceBase, +64) slice tickets, kS2TimeoutSlot a wait timeout, and
+// [kDownSliceBase, +511) slice tickets, [kDownPassBase, +511) slice-tail
+// counts, kS2TimeoutSlot a wait timeout, and
 // from kS2SyncBase one 128-byte line per split (its readiness count, then its
 // count of down workgroups past the wait).  Split s sits in 4 KB page s % 64,
 // line s / 64: the lines being polled at one time are 4 KB apart, so the
 // polls spread over the memory channels instead of queueing on one (one
 // packed run of counters slowed every gate/up row on that channel about 3x).
 constexpr int kDownSliceBase = 512;
+constexpr int kDownPassBase = 1024;
 constexpr int kS2TimeoutSlot = 1023;
 constexpr int kS2SyncBase = 4096;
 constexpr int kS2SyncPages = 64;

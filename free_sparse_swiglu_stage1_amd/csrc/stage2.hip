@@ -263,17 +263,35 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
 // order -- adds the residual if any, rounds and stores.
 // ------------------------------------------------------------------------
 
+constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
+
+// Waits (one thread) until *ctr >= target; false after kSpinTicks.
+__device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(8);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
+    }
+    return true;
+}
+
 // The end of a down-projection workgroup: its waves' accumulators are added
-// in LDS in wave order into this split's partial (coherent 64-bit stores);
-// the last split of the slice to finish (ticket) adds the partials --
-// interleaved groups of splits in parallel, each group in split order, then
-// the groups in order -- multiplies by the output row's FP8 scale if any
-// (dsc), adds the residual if any, rounds and stores.  V: columns per lane.
-template <typename T, int V, int NB, int NW>
+// in LDS in wave order into this split's partial (coherent 64-bit stores),
+// then it takes a ticket on its slice.  The last TG arrivals (TG when the
+// slice has at least TG splits, else 1) each finish one of TG column groups
+// of the slice: the earlier ones first wait until every split has arrived,
+// then each adds its columns' partials -- interleaved groups of splits in
+// parallel, each group in split order, then the groups in order --
+// multiplies by the output row's FP8 scale if any (dsc), adds the residual if
+// any, rounds and stores.  The last of them to finish resets the slice's
+// counters (slice_counter: arrivals; pass_counter: finished tails, TG > 1).
+// A wait that outlasts kSpinTicks sets *timeout_flag and goes on.
+template <typename T, int V, int NB, int NW, int TG>
 __device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&red)[NW][NB][64 * V], int *s_last,
                                             int sl, int s, int B, int d, int S, float *__restrict__ part,
                                             const float *__restrict__ dsc, const T *residual, T *out,
-                                            uint32_t *slice_counter)
+                                            uint32_t *slice_counter, uint32_t *pass_counter, uint32_t *timeout_flag)
 {
     constexpr int NT = 64 * NW;
     constexpr int COLS = 64 * V;
@@ -295,18 +313,30 @@ __device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&r
             store_agent2(&part[((int64_t)s * B + b) * d + col], v0, v1);
         }
     }
-    if (!publish_and_ticket(slice_counter, (uint32_t)S, s_last)) return;
-    // thread t: column pair t % (COLS/2) of the splits grp, grp + GROUPS,
-    // grp + 2*GROUPS, ... (grp = t / (COLS/2)); every load is one this thread
-    // needs, issued before any is added (the predicate is wave-uniform)
-    constexpr int PAIRS = COLS / 2;
-    constexpr int GROUPS = NT / PAIRS;
-    constexpr int QMAX = 36;  // splits per thread the loads cover in one batch (S <= 72: two batches)
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    __syncthreads();
+    if (tid == 0)
+        *s_last = (int)__hip_atomic_fetch_add(slice_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = uniform(*s_last);
+    const int ng = (TG > 1 && S >= TG) ? TG : 1;  // column groups of the tail
+    if (t < S - ng) return;
+    const int g = t - (S - ng);  // this workgroup's group
+    if (ng > 1 && t != S - 1) {  // not the last arrival: wait for the others
+        if (tid == 0 && !spin_wait_geq(slice_counter, (uint32_t)S))
+            __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+    }
+    // thread t: column pair t % PAIRS of this group, of the splits grp,
+    // grp + GROUPS, grp + 2*GROUPS, ... (grp = t / PAIRS); every load is one
+    // this thread needs, issued before any is added (wave-uniform predicate)
+    const int CG = COLS / ng, PAIRS = CG / 2, GROUPS = NT / PAIRS;
+    constexpr int QMAX = 36;  // splits per thread the loads cover in one batch
     const int pair = tid % PAIRS, grp = tid / PAIRS;
-    const int col0 = sl * COLS + pair * 2;
+    const int c0 = sl * COLS + g * CG;  // the group's first column
+    const int col0 = c0 + pair * 2;
     const int nq = (S - grp + GROUPS - 1) / GROUPS;  // this thread's splits
-    float (*gsum)[NB][COLS] = reinterpret_cast<float (*)[NB][COLS]>(&red[0][0][0]);  // [GROUPS][NB][COLS]
-    static_assert(GROUPS <= NW, "group sums must fit the reduction buffer");
+    float *gsum = &red[0][0][0];                     // [GROUPS][NB][CG]
     __syncthreads();
     const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * B * d));
     for (int b = 0; b < NB; ++b) {
@@ -327,19 +357,25 @@ __device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&r
                     }
             }
         }
-        gsum[grp][b][pair * 2] = y0;
-        gsum[grp][b][pair * 2 + 1] = y1;
+        gsum[(grp * NB + b) * CG + pair * 2] = y0;
+        gsum[(grp * NB + b) * CG + pair * 2 + 1] = y1;
     }
     __syncthreads();
-    for (int e = tid; e < B * COLS; e += NT) {
-        const int b = e / COLS, ci = e % COLS, col = sl * COLS + ci;
+    for (int e = tid; e < B * CG; e += NT) {
+        const int b = e / CG, ci = e % CG, col = c0 + ci;
         if (col >= d || b >= NB) continue;
-        float y = gsum[0][b][ci];
-#pragma unroll
-        for (int g = 1; g < GROUPS; ++g) y += gsum[g][b][ci];
+        float y = gsum[b * CG + ci];
+        for (int gg = 1; gg < GROUPS; ++gg) y += gsum[(gg * NB + b) * CG + ci];
         if (dsc) y *= dsc[col];
         if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
         elem<T>::store(out, (int64_t)b * d + col, y);
+    }
+    if (tid == 0) {  // the slice's counters back to zero once no one reads them
+        if (ng == 1 ||
+            __hip_atomic_fetch_add(pass_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)ng - 1) {
+            __hip_atomic_store(slice_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (ng > 1) __hip_atomic_store(pass_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -397,7 +433,8 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
         }
     }
 
-    down_finish<T, V, NB, NW>(acc, red, &s_last, sl, s, B, d, S, part, dsc, residual, out, &counters[sl]);
+    down_finish<T, V, NB, NW, 1>(acc, red, &s_last, sl, s, B, d, S, part, dsc, residual, out, &counters[sl], nullptr,
+                                 nullptr);
 }
 
 // ------------------------------------------------------------------------
@@ -423,18 +460,8 @@ constexpr int kS2Waves = 4;
 constexpr int kS2Rows = 16;                           // down rows per wave, all in flight
 constexpr int kS2Ranks = kS2Waves * kS2Rows;          // ranks per split
 constexpr int kS2GuPerSplit = kS2Ranks / 4;           // gate/up workgroups (4 ranks each) per split
-constexpr uint64_t kSpinTicks = 50000000ull;          // 0.5 s of the 100 MHz real-time counter
 
 // thread 0 only: waits until *ctr >= target; false on timeout
-__device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target)
-{
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(8);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
-    }
-    return true;
-}
 
 template <typename T, typename TW>
 __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
@@ -504,8 +531,9 @@ __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
             }
         }
     }
-    down_finish<T, V, 1, kS2Waves>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d,
-                                   S, part, dsc, residual, out, &counters[kDownSliceBase + sl]);
+    down_finish<T, V, 1, kS2Waves, 2>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d,
+                                      S, part, dsc, residual, out, &counters[kDownSliceBase + sl],
+                                      &counters[kDownPassBase + sl], &counters[kS2TimeoutSlot]);
 }
 
 // out = residual (or 0): the k == 0 case
