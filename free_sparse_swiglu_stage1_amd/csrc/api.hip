@@ -166,6 +166,9 @@ struct Workspace {
     int32_t *sel;
     float *s_sp;
     float *down_part;
+    float *gu_part;       // batches: gate/up chunk sums
+    uint16_t *s_pieces;   // batches: s as three bf16 pieces
+    float *bdn_part;      // batches: down split partials
     size_t bytes;
 };
 
@@ -191,6 +194,16 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     w.sel = (int32_t *)take(sizeof(int32_t) * F);
     w.s_sp = (float *)take(sizeof(float) * B * F);
     w.down_part = (float *)take(sizeof(float) * (size_t)down_s_max * 4 * d);
+    if (B > 1) {  // the matrix-core Stage 2 (bf16 activations)
+        const size_t tiles = (size_t)ceil_div(F, 16), chunks = (size_t)ceil_div(d, 1024);
+        w.gu_part = (float *)take(sizeof(float) * tiles * chunks * 512);
+        w.s_pieces = (uint16_t *)take(sizeof(uint16_t) * 3 * 16 * (size_t)(ceil_div(F, 32) * 32));
+        w.bdn_part = (float *)take(sizeof(float) * (size_t)batch_max_splits((int)d, (int)F) * B * d);
+    } else {
+        w.gu_part = nullptr;
+        w.s_pieces = nullptr;
+        w.bdn_part = nullptr;
+    }
     w.bytes = off;
     return w;
 }
@@ -250,6 +263,14 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
     if (B == 1) {  // one launch: the down projection starts while gate/up drains
         TRY_HIP(launch_stage2_fused(dt, sw, x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part, residual,
                                     out, ws.counters, iota_out, st));
+        TRY_HIP(mark(ev, 4, st));
+        return hip_status(mark(ev, 5, st));
+    }
+    if (dt == 1) {  // bf16 activations: gate/up and down on the matrix cores
+        const BatchPlan bp = batch_plan((int)d, (int)k, (int)B, sw.fmt);
+        TRY_HIP(launch_stage2_batch(sw, x, (int)B, (int)d, (int)w->d_ff, sel, (int)k, bp, ws.gu_part, ws.s_pieces,
+                                    ws.bdn_part, residual, out, ws.counters + kS2SyncBase,
+                                    ws.counters + kDownSliceBase, iota_out, st));
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }

@@ -37,6 +37,18 @@ struct DownPlan {
     int nb;         // tokens per pass
 };
 
+// Stage 2 for batches of 2..16 tokens, bf16 activations, on the matrix
+// cores (stage2_batch.hip).
+struct BatchPlan {
+    int n_tiles;  // gate/up tiles of 16 channels
+    int SK;       // gate/up input chunks
+    int KW;       // inputs per chunk (a multiple of 1024)
+    int KP;       // k rounded up to 32 (ranks of the s pieces)
+    int n_ct;     // down column tiles (128 bytes of a row: 64 bf16 or 128 FP8 columns)
+    int S;        // down rank splits
+    int kps;      // down K-steps (32 ranks) per split
+};
+
 // Single-token Stage 1 in one kernel (stage1_fused.hip).
 constexpr int kFusedMaxD = 8192;       // inputs (d_model)
 constexpr int kFusedMaxF = 16384;      // channels (d_ff): all scores fit in LDS
@@ -87,6 +99,16 @@ hipError_t launch_gateup(int dtype, const S2Weights &w, const void *x, int B, in
 hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const float *s_sp, int B, int k,
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
+// Stage 2 for batches (stage2_batch.hip).
+BatchPlan batch_plan(int d, int k, int B, int fp8);
+int batch_max_splits(int d, int F);  // the largest BatchPlan::S over k <= F
+// gu_part: n_tiles*SK*512 floats; s_pieces: 3*16*KP bf16; dn_part: S*B*d
+// floats; gu_counters: n_tiles words, dn_counters: n_ct words, zero on entry
+// and left zero.
+hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, int F, const int32_t *sel, int k,
+                               const BatchPlan &pl, float *gu_part, uint16_t *s_pieces, float *dn_part,
+                               const void *residual, void *out, uint32_t *gu_counters, uint32_t *dn_counters,
+                               int32_t *iota_out, hipStream_t st);
 // Stage 2 for one token in one launch (stage2.hip).  Counter slots:
 // [kDownSliceBase, +511) slice tickets, [kDownPassBase, +511) slice-tail
 // counts, kS2TimeoutSlot a wait timeout, and

@@ -386,7 +386,6 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
                                                        float *__restrict__ part, const T *residual, T *out,
                                                        uint32_t *__restrict__ counters)
 {
-    constexpr int NT = 64 * NW;
     constexpr int V = WRows<TW>::DV;
     constexpr int COLS = 64 * V;
     constexpr int U = kDownRowsPerWave;
