@@ -178,6 +178,7 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
 {
     const ProxyPlan pp = proxy_plan(d, F, B, mode);
     size_t part_rows = (size_t)pp.S * B;
+    if ((size_t)proxy_batch_splits((int)d) * B > part_rows) part_rows = (size_t)proxy_batch_splits((int)d) * B;
     if (fused_supported(B, d, F)) {
         const FusedPlan fp = fused_plan(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
         if ((size_t)fp.S > part_rows) part_rows = fp.S;
@@ -239,8 +240,12 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
     TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
                            kTicketWords, st));
     TRY_HIP(mark(ev, 1, st));
-    TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes, (const float *)p->scales,
-                         ws.proxy_part, score, ws.counters, o.act, o.signal, st));
+    if (dt == 1 && p->mode == PROX_Q_INT8_ROW && B > 1)  // bf16 batches, int8 codes: the matrix cores
+        TRY_HIP(launch_proxy_batch(ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes,
+                                   (const float *)p->scales, ws.proxy_part, score, ws.counters, o.act, o.signal, st));
+    else
+        TRY_HIP(launch_proxy(pp, ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes,
+                             (const float *)p->scales, ws.proxy_part, score, ws.counters, o.act, o.signal, st));
     TRY_HIP(mark(ev, 2, st));
     if (k > 0) TRY_HIP(launch_topk(score, (int)F, (int)k, sel, st));
     return PROX_OK;

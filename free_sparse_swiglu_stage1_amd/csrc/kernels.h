@@ -99,6 +99,13 @@ hipError_t launch_gateup(int dtype, const S2Weights &w, const void *x, int B, in
 hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const float *s_sp, int B, int k,
                        const int32_t *sel, int d, int F, float *part, const void *residual, void *out,
                        uint32_t *counters, hipStream_t st);
+// The proxy for batches of 2..16 bf16 tokens with int8 codes, on the matrix
+// cores (stage1_batch.hip): scores from xh[B][d] (the kept inputs, zeros
+// elsewhere).  part: proxy_batch_splits(d)*B*2*F floats; counters [0, F/128)
+// zero on entry and left zero.
+int proxy_batch_splits(int d);
+hipError_t launch_proxy_batch(const float *xh, int B, int d, int F, const uint8_t *codes, const float *scales,
+                              float *part, float *score, uint32_t *counters, int act, int signal, hipStream_t st);
 // Stage 2 for batches (stage2_batch.hip).
 BatchPlan batch_plan(int d, int k, int B, int fp8);
 int batch_max_splits(int d, int F);  // the largest BatchPlan::S over k <= F
