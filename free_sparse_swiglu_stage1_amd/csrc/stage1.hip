@@ -12,7 +12,8 @@ namespace prox {
 // ------------------------------------------------------------------------
 // K1a: per-token input sparsification.  One workgroup per token keeps the
 // k_in largest |x_i| (ties: lower i) and writes the sparse copy xh[b][d]
-// (fp32, zeros elsewhere).  Block 0 also clears the workspace counters the
+// (fp32, zeros elsewhere); with no tie at the threshold T the kept set is
+// simply |x_i| >= T.  Block 0 also clears the workspace counters the
 // later kernels of the same call use.
 // ------------------------------------------------------------------------
 template <typename T, int KPT>
@@ -37,9 +38,19 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
         if (slot_index<KPT>(r) >= d) v[r] = 0.0f;
         key[r] = __float_as_uint(v[r]) & 0x7FFFFFFFu;
     }
-    const SelectResult sr = block_select<1024, KPT>(key, d, k_in, sm);
-    selection_bitmap<1024, KPT>(key, d, sr, sm);
+    // magnitudes are sign-free, and a bf16 value's low 16 bits are zero
+    const SelectResult sr = block_select_window<1024, KPT>(key, d, k_in, 30, sizeof(T) == 2 ? 16 : 0, sm);
     float *ob = xh + (int64_t)b * d;
+    if (uniform_u32(sr.need_eq) == uniform_u32(sr.count_eq)) {  // no tie to break: keep key >= T
+        const uint32_t thr = uniform_u32(sr.T);
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int i = slot_index<KPT>(r);
+            if (i < d) ob[i] = key[r] >= thr ? v[r] : 0.0f;
+        }
+        return;
+    }
+    selection_bitmap<1024, KPT>(key, d, sr, sm);
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
         const int i = slot_index<KPT>(r);
@@ -280,8 +291,9 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
 
 // ------------------------------------------------------------------------
 // K2: top-k channel mask.  One workgroup of 1024 threads: radix select of the
-// k-th largest |score| bit pattern, then an ordered compaction that writes the
-// selected channel indices in ascending order.
+// k-th largest |score| bit pattern, then the selected channel indices in
+// ascending order (one ballot per row when no tie is broken at the
+// threshold, else an ordered compaction of the selection bitmap).
 // ------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ score, int n, int k,
@@ -294,9 +306,15 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ sc
         const int i = slot_index<KPT>(r);
         key[r] = __float_as_uint(score[i < n ? i : n - 1]);
     }
+    // slots past n get the key 0xFFFFFFFF, which no selection step takes
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) key[r] = (slot_index<KPT>(r) < n) ? (key[r] & 0x7FFFFFFFu) : 0u;
-    const SelectResult sr = block_select<1024, KPT>(key, n, k, sm);
+    for (int r = 0; r < KPT; ++r) key[r] = (slot_index<KPT>(r) < n) ? (key[r] & 0x7FFFFFFFu) : 0xFFFFFFFFu;
+    // scores are sign-free: the window is bits 30..0
+    const SelectResult sr = block_select_window<1024, KPT>(key, n, k, 30, 0, sm);
+    if (uniform_u32(sr.need_eq) == uniform_u32(sr.count_eq)) {  // no tie to break: key >= T
+        emit_at_least<1024, KPT>(key, uniform_u32(sr.T), sel, (uint32_t)k, sm);
+        return;
+    }
     selection_bitmap<1024, KPT>(key, n, sr, sm);
     emit_bitmap<1024>(n, sm, [&](int i, uint32_t pos) {
         if (pos < (uint32_t)k) sel[pos] = i;
