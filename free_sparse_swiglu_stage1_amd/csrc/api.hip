@@ -240,7 +240,9 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
     TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
                            kTicketWords, st));
     TRY_HIP(mark(ev, 1, st));
-    if (dt == 1 && p->mode == PROX_Q_INT8_ROW && B > 1)  // bf16 batches, int8 codes: the matrix cores
+    // bf16 batches above 4 tokens, int8 codes: the matrix cores (at 4 tokens
+    // the vector-ALU kernel is faster, 32.6 against 35.3 us at 4096 x 14336)
+    if (dt == 1 && p->mode == PROX_Q_INT8_ROW && B > 4)
         TRY_HIP(launch_proxy_batch(ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes,
                                    (const float *)p->scales, ws.proxy_part, score, ws.counters, o.act, o.signal, st));
     else

@@ -309,8 +309,9 @@ hipError_t launch_proxy_batch(const float *xh, int B, int d, int F, const uint8_
                               float *part, float *score, uint32_t *counters, int act, int signal, hipStream_t st)
 {
     if (B < 2 || B > 16 || F % 16 != 0) return hipErrorInvalidValue;
-    const int S = proxy_batch_splits(d);
-    const int R = (d + S - 1) / S;
+    // splits of a multiple of 32 inputs: the prologue reads 4 at a time
+    const int R = ((d + proxy_batch_splits(d) - 1) / proxy_batch_splits(d) + 31) / 32 * 32;
+    const int S = (d + R - 1) / R;
     const int n_cb = (F + kPxCh - 1) / kPxCh;
     if (R > kPxMaxR || n_cb > kFusedScoreSlot) return hipErrorInvalidValue;
     proxy_batch_kernel<<<dim3(n_cb, S), 256, 0, st>>>(xh, B, d, F, codes, scales, R, S, part, score, counters, act,

@@ -112,6 +112,10 @@ def _tied_x(B, d, dtype, seed):
     # tied input magnitudes
     (1024, 2064, "bf16", 1, "int8_row", "xties"), (2048, 4096, "f32", 1, "int8_row", "xties"),
     (768, 1040, "bf16", 2, "int8_row", "xties"),
+    # the matrix-core proxy (bf16, more than 4 tokens): ties, and input splits
+    # of a length that is not a multiple of 1024 (d = 2504: three splits of 864)
+    (1024, 2064, "bf16", 6, "int8_row", "dup"), (768, 1040, "bf16", 8, "int8_row", "zeros"),
+    (2504, 1040, "bf16", 8, "int8_row", None), (768, 1040, "bf16", 5, "int8_row", "xties"),
 ])
 def test_stage1_scores_and_mask(d, F, dtype, B, mode, pattern):
     L = Layer(d, F, 0.02, dtype, seed=11, pattern=pattern if pattern != "xties" else None)
