@@ -157,8 +157,13 @@ __device__ __forceinline__ void pipeline2(int n, Buf &A, Buf &B, Issue issue, Co
 // streams at about half the rate of 4 rows per instruction, so the rows are
 // loaded 4 at a time -- lanes 16 q' .. 16 q' + 15 read 256 contiguous bytes
 // of row 4 q + q' -- and regrouped through a per-wave LDS tile (gate, then
-// up).  MFMA step t of a sub-chunk takes inputs 32 t + 8 g .. + 7 in lane
-// group g = l / 16.  x (B) is read from L2; token slots >= B read zeros.
+// up).  Above 8 tokens x is read from L2 the same way, 4 tokens per
+// instruction, and regrouped through a second tile: read as MFMA operands,
+// 16 tokens per instruction, it cost 4.7 us of 22 at B = 16; at 4 tokens the
+// extra LDS round trip costs more than it saves, and x is read as operands
+// (token slots >= B read zeros either way).
+// MFMA step t of a sub-chunk takes inputs 32 t + 8 g .. + 7 in lane group
+// g = l / 16.
 // ------------------------------------------------------------------------
 template <typename TW>
 struct GuRowsB;
@@ -180,7 +185,7 @@ template <> struct GuRowsB<uint8_t> {  // FP8: a sub-chunk row is 256 B, one 16-
     }
 };
 
-template <typename TW>
+template <typename TW, bool XTILE>
 __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restrict__ x, int B, int d, int F,
                                                        const TW *__restrict__ w_gu, const float *__restrict__ gsc,
                                                        const int32_t *__restrict__ sel, int k, int SK, int KW,
@@ -192,7 +197,9 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
     constexpr int LPR = GuRowsB<TW>::LPR;
     constexpr int PITCH = GuRowsB<TW>::PITCH;
     constexpr int NLW = 4 * LPR;          // weight loads per half per sub-chunk
+    constexpr int XPITCH = 528;  // LDS bytes per token row of a sub-chunk (256 bf16 + 16-byte pad)
     __shared__ __align__(16) uint8_t tiles[kGuWaves][16 * PITCH];
+    __shared__ __align__(16) uint8_t xtiles[XTILE ? kGuWaves : 1][XTILE ? 16 * XPITCH : 16];
     __shared__ __align__(16) float red[kGuWaves * 2 * 64 * 4];
     __shared__ int s_last;
 
@@ -201,6 +208,7 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
     const int kc = blockIdx.x, tile = blockIdx.y;
     const int c0 = kc * KW, c1 = min(d, c0 + KW);
     uint8_t *my = tiles[wv];
+    uint8_t *myx = xtiles[wv];
 
     // lane l loads rows 4 q + g (q = 0..3) of the tile (ranks past k repeat
     // rank k - 1; not stored)
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
     const int rr = tile * 16 + li;
     if (iota_out && kc == 0 && wv == 0 && g == 0 && rr < k) iota_out[rr] = rr;
     const ZeroBuf xb(x, (uint32_t)(2u * B * d));
-    const uint32_t xrow = li < B ? (uint32_t)(2 * li * d) : xb.end;  // token slots >= B: zeros
+    constexpr bool xtile = XTILE;  // x through the LDS tile (else read as operands)
 
     struct Buf {
         u32x4 wg[NLW], wu[NLW], xv[8];
@@ -232,10 +240,15 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
                 b.wu[q * LPR + p] = ld_stream(grow[q] + d + ic);
             }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int i = ib + 32 * t + 8 * g;
-            b.xv[t] = xb.load16(i < c1 && xrow != xb.end ? xrow + (uint32_t)(2 * i) : xb.end);
-        }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                // tile: tokens 4 q + g, 256 contiguous bytes each; operands:
+                // token li, inputs 32 t + 8 g (t = 2 q + p)
+                const int tok = xtile ? 4 * q + g : li;
+                const int i = ib + (xtile ? p * 128 + 8 * li : 32 * (2 * q + p) + 8 * g);
+                b.xv[q * 2 + p] = xb.load16(tok < B && i < c1 ? (uint32_t)(2 * (tok * d + i)) : xb.end);
+            }
     };
     f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
     auto half = [&](const u32x4 (&w)[NLW], const u32x4 (&xv)[8], f32x4 &acc) {
@@ -249,8 +262,23 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
         for (int t = 0; t < 8; ++t) acc = mfma16(GuRowsB<TW>::operand(rowp, t, g), xv[t], acc);
     };
     auto compute = [&](const Buf &b) {
-        half(b.wg, b.xv, ag);
-        half(b.wu, b.xv, au);
+        if constexpr (xtile) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    *reinterpret_cast<u32x4 *>(myx + (4 * q + g) * XPITCH + (p * 128 + 8 * li) * 2) =
+                        b.xv[q * 2 + p];
+            u32x4 xo[8];  // the MFMA B operands: token li, inputs 32 t + 8 g .. + 7
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                xo[t] = *reinterpret_cast<const u32x4 *>(myx + li * XPITCH + (32 * t + 8 * g) * 2);
+            half(b.wg, xo, ag);
+            half(b.wu, xo, au);
+        } else {
+            half(b.wg, b.xv, ag);
+            half(b.wu, b.xv, au);
+        }
     };
     Buf b0, b1;
     const int nsub = uniform(ibw < c1 ? (c1 - ibw + kGuWaves * kGuWaveK - 1) / (kGuWaves * kGuWaveK) : 0);
@@ -551,15 +579,18 @@ hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, 
     if (pl.kps > kDnMaxKps || pl.n_ct > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
     const dim3 ggrid(pl.SK, pl.n_tiles), dgrid(pl.S, pl.n_ct);
     const uint16_t *xp = (const uint16_t *)x;
+    // x through the LDS tile above 8 tokens (see gu_batch_kernel)
+#define GU(TW, XT, SC)                                                                                          \
+    gu_batch_kernel<TW, XT><<<ggrid, 256, 0, st>>>(xp, B, d, F, (const TW *)w.w_gu, SC, sel, k, pl.SK, pl.KW,   \
+                                                   gu_part, gu_counters, s_pieces, pl.KP, w.act, iota_out)
     if (w.fmt == 1) {
-        gu_batch_kernel<uint8_t><<<ggrid, 256, 0, st>>>(xp, B, d, F, (const uint8_t *)w.w_gu, w.gu_scales, sel, k,
-                                                        pl.SK, pl.KW, gu_part, gu_counters, s_pieces, pl.KP, w.act,
-                                                        iota_out);
+        if (B > 8) GU(uint8_t, true, w.gu_scales);
+        else GU(uint8_t, false, w.gu_scales);
     } else {
-        gu_batch_kernel<uint16_t><<<ggrid, 256, 0, st>>>(xp, B, d, F, (const uint16_t *)w.w_gu, nullptr, sel, k,
-                                                         pl.SK, pl.KW, gu_part, gu_counters, s_pieces, pl.KP, w.act,
-                                                         iota_out);
+        if (B > 8) GU(uint16_t, true, nullptr);
+        else GU(uint16_t, false, nullptr);
     }
+#undef GU
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (w.fmt == 1) {
