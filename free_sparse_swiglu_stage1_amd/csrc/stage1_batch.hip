@@ -102,44 +102,31 @@ __global__ __launch_bounds__(256) void proxy_batch_kernel(const float *__restric
     const int c0 = cb * kPxCh;
 
     // ---- prologue: the inputs of [i0, i1) some token kept, and their x.
-    // Thread t reads inputs i0 + 4t .. + 3 of every token, 8 tokens per batch
-    // of 16-byte loads (past i1 or past the tokens: zeros): once for the
-    // kept set, once more (from L2) to lay the kept inputs' x out.
+    // Thread t reads inputs i0 + 4t .. + 3 of every token, all 16-byte loads
+    // issued at once (past i1 or past the tokens: zeros), and keeps them for
+    // the layout below.
     const ZeroBuf xb(xh, (uint32_t)(4u * B * d));
     const int ix = i0 + 4 * tid;
-    auto load8 = [&](int b0, u32x4 (&v)[8]) {
+    u32x4 xv[16];
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
-            v[b] = xb.load16(b0 + b < B && ix < i1 ? (uint32_t)(4 * ((b0 + b) * d + ix)) : xb.end);
-    };
-    uint32_t keep = 0;  // bit q: input i0 + 4 tid + q is kept by some token
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-        u32x4 v[8];
-        load8(8 * h, v);
+    for (int b = 0; b < 16; ++b)
+        xv[b] = xb.load16(b < B && ix < i1 ? (uint32_t)(4 * (b * d + ix)) : xb.end);
+    uint32_t keep = 0;  // bit q: input ix + q is kept by some token (+0 and -0 are not)
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < 16; ++b)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) keep |= ((v[b][q] << 1) != 0u ? 1u : 0u) << q;  // +0 and -0 are not kept
-    }
+        for (int q = 0; q < 4; ++q) keep |= ((xv[b][q] << 1) != 0u ? 1u : 0u) << q;
     uint32_t tot;
-    const int p0 = (int)block_excl_scan<256>((uint32_t)__popc(keep), scr, &tot);
+    int p = (int)block_excl_scan<256>((uint32_t)__popc(keep), scr, &tot);
     const int nk = (int)tot;
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-        u32x4 v[8];
-        __builtin_amdgcn_sched_barrier(0);
-        load8(8 * h, v);
-        int p = p0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (keep & (1u << q)) {
-                if (h == 0) lst[p] = ix + q;
+    for (int q = 0; q < 4; ++q)
+        if (keep & (1u << q)) {
+            lst[p] = ix + q;
 #pragma unroll
-                for (int b = 0; b < 8; ++b) xt[p >> 5][(p >> 3) & 3][8 * h + b][p & 7] = (uint16_t)(v[b][q] >> 16);
-                ++p;
-            }
-    }
+            for (int b = 0; b < 16; ++b) xt[p >> 5][(p >> 3) & 3][b][p & 7] = (uint16_t)(xv[b][q] >> 16);
+            ++p;
+        }
     const int nk32 = (nk + 31) & ~31;  // the last K-step padded with input i0 and x = 0
     for (int p = nk + tid; p < nk32; p += 256) {
         lst[p] = i0;
@@ -222,25 +209,33 @@ __global__ __launch_bounds__(256) void proxy_batch_kernel(const float *__restric
     // ---- the four waves' sums: (w0 + w2) + (w1 + w3), through LDS.
     // a[c][r]: channel 8 (4 g + r) + c of the block, token li
     __syncthreads();  // x no longer read
+    // (register r of MFMA c: channels 8 (4 g + r) + c, c = 0..7 contiguous)
     auto put = [&](int slot) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int ci = 8 * (4 * g + r) + c;
-                red[((slot * 16 + li) * 2 + 0) * kPxCh + ci] = ag[c][r];
-                red[((slot * 16 + li) * 2 + 1) * kPxCh + ci] = au[c][r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            float *dg = &red[((slot * 16 + li) * 2 + 0) * kPxCh + 8 * (4 * g + r)];
+            float *du = dg + kPxCh;
+            *reinterpret_cast<f32x4 *>(dg) = f32x4{ag[0][r], ag[1][r], ag[2][r], ag[3][r]};
+            *reinterpret_cast<f32x4 *>(dg + 4) = f32x4{ag[4][r], ag[5][r], ag[6][r], ag[7][r]};
+            *reinterpret_cast<f32x4 *>(du) = f32x4{au[0][r], au[1][r], au[2][r], au[3][r]};
+            *reinterpret_cast<f32x4 *>(du + 4) = f32x4{au[4][r], au[5][r], au[6][r], au[7][r]};
+        }
     };
     auto add = [&](int slot) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+            const float *dg = &red[((slot * 16 + li) * 2 + 0) * kPxCh + 8 * (4 * g + r)];
+            const float *du = dg + kPxCh;
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(dg), g1 = *reinterpret_cast<const f32x4 *>(dg + 4);
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(du), u1 = *reinterpret_cast<const f32x4 *>(du + 4);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int ci = 8 * (4 * g + r) + c;
-                ag[c][r] += red[((slot * 16 + li) * 2 + 0) * kPxCh + ci];
-                au[c][r] += red[((slot * 16 + li) * 2 + 1) * kPxCh + ci];
+            for (int c = 0; c < 4; ++c) {
+                ag[c][r] += g0[c];
+                ag[c + 4][r] += g1[c];
+                au[c][r] += u0[c];
+                au[c + 4][r] += u1[c];
             }
+        }
     };
     if (wv >= 2) put(wv - 2);
     __syncthreads();
@@ -256,41 +251,49 @@ __global__ __launch_bounds__(256) void proxy_batch_kernel(const float *__restric
     // red[0][b][h][ci]: the workgroup's g~ (h = 0) and u~ (h = 1), unscaled
 
     if (S > 1) {
-        // element e = (b, h, ci) of the block: thread t owns e = t + 256 m
-        for (int e = tid; e < B * 2 * kPxCh; e += 256) {
-            const int b = e / (2 * kPxCh), h = (e / kPxCh) & 1, ci = e % kPxCh, j = c0 + ci;
-            if (j < F) store_agent(&part[(((int64_t)s * B + b) * 2 + h) * F + j], red[e]);
+        // element pairs e, e + 1 = (b, h, ci) of the block, e = 2 (t + 256 m):
+        // 64-bit coherent stores, and for the last split 64-bit coherent
+        // loads, every split's in one batch, added in split order
+        constexpr int MP = 16 * 2 * kPxCh / 2 / 256;  // pairs per thread at 16 tokens
+        for (int m = 0; m < MP; ++m) {
+            const int e = 2 * (tid + 256 * m);
+            const int b = e / (2 * kPxCh), h = (e / kPxCh) & 1, j = c0 + e % kPxCh;
+            if (b < B && j < F) store_agent2(&part[(((int64_t)s * B + b) * 2 + h) * F + j], red[e], red[e + 1]);
         }
         if (!publish_and_ticket(&counters[cb], (uint32_t)S, &s_last)) return;
-        // the splits' partials of the thread's elements, 2 splits per batch of
-        // loads (all issued before any is added), added in split order
         const ZeroBuf pb(part, (uint32_t)(4u * S * B * 2 * F));
-        float acc[16];
+        float acc[MP][2];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-        for (int q0 = 0; q0 < S; q0 += 2) {
-            float v[2][16];
+        for (int m = 0; m < MP; ++m) acc[m][0] = acc[m][1] = 0.0f;
+        for (int q0 = 0; q0 < S; q0 += 4) {
+            u32x2 v[4][MP];
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const int e = tid + 256 * m;
+                for (int m = 0; m < MP; ++m) {
+                    const int e = 2 * (tid + 256 * m);
                     const int b = e / (2 * kPxCh), h = (e / kPxCh) & 1, j = c0 + e % kPxCh;
                     const bool ok = q0 + q < S && b < B && j < F;
                     const uint32_t off = ok ? (uint32_t)(4 * ((((q0 + q) * B + b) * 2 + h) * F + j)) : pb.end;
-                    v[q][m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pb.rsrc, (int)off, 0,
-                                                                                   CoherentBuf::kSc1));
+                    v[q][m] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(pb.rsrc, (int)off, 0, CoherentBuf::kSc1));
                 }
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (q0 + q < S) acc[m] += v[q][m];
+                for (int m = 0; m < MP; ++m)
+                    if (q0 + q < S) {
+                        acc[m][0] += __uint_as_float(v[q][m][0]);
+                        acc[m][1] += __uint_as_float(v[q][m][1]);
+                    }
         }
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
-            if (tid + 256 * m < B * 2 * kPxCh) red[tid + 256 * m] = acc[m];
+        for (int m = 0; m < MP; ++m) {
+            const int e = 2 * (tid + 256 * m);
+            red[e] = acc[m][0];
+            red[e + 1] = acc[m][1];
+        }
         __syncthreads();
     }
     // ---- scores of the block's channels (thread t < 128: channel c0 + t)
