@@ -91,9 +91,14 @@ def algorithmic_bytes(d, F, B, k, k_union, bw, mode, fp8=False):
                 down=k * d * ww + (4 * d if fp8 and k else 0), sel=k * 4, out=B * d * bw)
 
 
+# the sources the single-token kernels (stage1_fused_kernel, stage2_fused_kernel)
+# are built from: the stored counter traffic is valid while these are unchanged
+DIGEST_SOURCES = ("common.h", "kernels.h", "select.h", "stage1_fused.hip", "stage2.hip")
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "free_sparse_swiglu_stage1_amd", "csrc"))):
+    for f in DIGEST_SOURCES:
         with open(os.path.join(ROOT, "free_sparse_swiglu_stage1_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
