@@ -41,7 +41,8 @@ struct DownPlan {
 // cores (stage2_batch.hip).
 struct BatchPlan {
     int n_tiles;  // gate/up tiles of 16 channels
-    int SK;       // gate/up input chunks
+    int n_full;   // gate/up tiles run whole, one workgroup each (a multiple of the CU count)
+    int SK;       // input chunks of each other tile
     int KW;       // inputs per chunk (a multiple of 1024)
     int KP;       // k rounded up to 32 (ranks of the s pieces)
     int n_ct;     // down column tiles (128 bytes of a row: 64 bf16 or 128 FP8 columns)

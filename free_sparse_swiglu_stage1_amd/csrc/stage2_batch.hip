@@ -148,9 +148,13 @@ __device__ __forceinline__ void pipeline2(int n, Buf &A, Buf &B, Issue issue, Co
 }  // namespace
 
 // ------------------------------------------------------------------------
-// Gate/up.  Grid (SK input chunks of KW, ceil(k/16) tiles); 4 waves.  SK is 1
-// unless the tiles alone are too few to fill the chip.  Wave w takes the
-// 256-input sub-chunks w, w + 4, ... of its chunk, two in flight.
+// Gate/up.  1-D grid: tiles [0, n_full) whole, one workgroup each, then the
+// tiles [n_full, ceil(k/16)) in SK input chunks of KW each; 4 waves.  n_full
+// is a multiple of the CU count, so the whole tiles take one workgroup slot
+// on every CU and the chunks of the rest fill second slots evenly (269
+// whole tiles on 256 CUs left 13 CUs with two, which ended at 16 us against
+// a median of 9.3).  Wave w takes the 256-input sub-chunks w, w + 4, ... of
+// its range, two in flight.
 //
 // The MFMA wants channel l % 16 of the tile in lane l (A) and token l % 16
 // (B).  Loading A that way makes each load instruction touch 16 rows, which
@@ -188,7 +192,8 @@ template <> struct GuRowsB<uint8_t> {  // FP8: a sub-chunk row is 256 B, one 16-
 template <typename TW, bool XTILE>
 __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restrict__ x, int B, int d, int F,
                                                        const TW *__restrict__ w_gu, const float *__restrict__ gsc,
-                                                       const int32_t *__restrict__ sel, int k, int SK, int KW,
+                                                       const int32_t *__restrict__ sel, int k, int n_full, int SK,
+                                                       int KW,
                                                        float *__restrict__ part, uint32_t *__restrict__ counters,
                                                        uint16_t *__restrict__ sp, int KP, int act,
                                                        int32_t *__restrict__ iota_out)
@@ -205,8 +210,10 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
 
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int kc = blockIdx.x, tile = blockIdx.y;
-    const int c0 = kc * KW, c1 = min(d, c0 + KW);
+    const int L = blockIdx.x, split = L >= n_full;
+    const int tile = split ? n_full + (L - n_full) / SK : L;
+    const int kc = split ? (L - n_full) % SK : 0;
+    const int c0 = kc * KW, c1 = split ? min(d, c0 + KW) : d;
     uint8_t *my = tiles[wv];
     uint8_t *myx = xtiles[wv];
 
@@ -290,11 +297,11 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
     // thread t: gate (v0) and up (v1) of lane t / 4's register t % 4
     float v0 = ((red[tid] + red[512 + tid]) + red[1024 + tid]) + red[1536 + tid];
     float v1 = ((red[256 + tid] + red[768 + tid]) + red[1280 + tid]) + red[1792 + tid];
-    if (SK > 1) {
-        float *pp = part + ((int64_t)tile * SK + kc) * 512;
+    if (split && SK > 1) {
+        float *pp = part + ((int64_t)(tile - n_full) * SK + kc) * 512;
         store_agent2(&pp[2 * tid], v0, v1);
         if (!publish_and_ticket(&counters[tile], (uint32_t)SK, &s_last)) return;
-        const ZeroBuf pb(part + (int64_t)tile * SK * 512, (uint32_t)(4 * SK * 512));
+        const ZeroBuf pb(part + (int64_t)(tile - n_full) * SK * 512, (uint32_t)(4 * SK * 512));
         v0 = v1 = 0.0f;
         for (int q0 = 0; q0 < SK; q0 += 8) {
             float a[8], b[8];
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
     sp[(2 * kBT + tok) * (int64_t)KP + rank] = p2;
     // the last tile also clears the ranks up to KP
     const int rz = (tile + 1) * 16 + (tid >> 4);
-    if (tile == (int)gridDim.y - 1 && rz < KP) {
+    if (tile == (k + 15) / 16 - 1 && rz < KP) {
 #pragma unroll
         for (int p = 0; p < 3; ++p) sp[(p * kBT + (tid & 15)) * (int64_t)KP + rz] = 0;
     }
@@ -535,14 +542,13 @@ BatchPlan batch_plan(int d, int k, int B, int fp8)
 {
     BatchPlan p;
     p.n_tiles = (k + 15) / 16;
-    // input chunks only when the tiles alone give fewer than 1024 waves
-    const int chunks_max = (d + kGuWaves * kGuWaveK - 1) / (kGuWaves * kGuWaveK);
-    int sk = (1024 + 4 * p.n_tiles - 1) / (4 * p.n_tiles);
-    if (sk > chunks_max) sk = chunks_max;
-    if (sk < 1) sk = 1;
+    // whole tiles in multiples of the CU count; the rest in input chunks of
+    // 1024 (one per wave of 4 x 256), which spread evenly over the CUs
+    constexpr int kCUs = 256;
     const int unit = kGuWaves * kGuWaveK;
-    p.KW = ((d + sk - 1) / sk + unit - 1) / unit * unit;
-    p.SK = (d + p.KW - 1) / p.KW;
+    p.n_full = p.n_tiles / kCUs * kCUs;
+    p.KW = unit;
+    p.SK = (d + unit - 1) / unit;
     p.KP = (k + 31) / 32 * 32;
     const int KS = p.KP / 32;
     const int cols = fp8 ? 128 : 64;
@@ -577,11 +583,12 @@ hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, 
 {
     if (k <= 0 || B < 2 || B > kBT) return hipErrorInvalidValue;
     if (pl.kps > kDnMaxKps || pl.n_ct > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
-    const dim3 ggrid(pl.SK, pl.n_tiles), dgrid(pl.S, pl.n_ct);
+    const dim3 ggrid(pl.n_full + (pl.n_tiles - pl.n_full) * pl.SK), dgrid(pl.S, pl.n_ct);
     const uint16_t *xp = (const uint16_t *)x;
     // x through the LDS tile above 8 tokens (see gu_batch_kernel)
 #define GU(TW, XT, SC)                                                                                          \
-    gu_batch_kernel<TW, XT><<<ggrid, 256, 0, st>>>(xp, B, d, F, (const TW *)w.w_gu, SC, sel, k, pl.SK, pl.KW,   \
+    gu_batch_kernel<TW, XT><<<ggrid, 256, 0, st>>>(xp, B, d, F, (const TW *)w.w_gu, SC, sel, k, pl.n_full, pl.SK, \
+                                                   pl.KW,                                                        \
                                                    gu_part, gu_counters, s_pieces, pl.KP, w.act, iota_out)
     if (w.fmt == 1) {
         if (B > 8) GU(uint8_t, true, w.gu_scales);
