@@ -13,7 +13,7 @@
 //                    the chunks' sums in chunk order) and writes s = act(g) u
 //                    as three bf16 pieces (below).
 //  dn_batch_kernel   y[b][m] = sum_r s[b][r] W_down^T[sel[r]][m] over 128
-//                    bytes of columns per workgroup and a range of ranks; the
+//                    columns per workgroup and a range of ranks; the
 //                    last rank split of a column tile (ticket) adds the
 //                    splits' partials in split order, scales (FP8), adds the
 //                    residual and rounds.
@@ -46,6 +46,7 @@ constexpr int kGuK = kGuWaves * kGuWaveK;    // inputs per gate/up workgroup
 constexpr int kXPitch = kGuK + 8;            // LDS x row, bf16 elements (16-byte pad: no bank conflicts)
 constexpr int kDnWaves = 8;                  // waves per down workgroup
 constexpr int kDnCols = 128;                 // output columns per down workgroup
+constexpr int kDnTargetWgs = 256;           // down workgroups aimed at (column tiles x rank splits)
 constexpr int kDnMaxKps = 64;                // K-steps (32 ranks) per down workgroup, at most
 
 // D[i][j] += sum_k A[i][k] B[k][j], 16 x 16 x 32.  Lane l holds A row l % 16
@@ -347,22 +348,25 @@ __global__ __launch_bounds__(256) void gu_batch_kernel(const uint16_t *__restric
 
 // ------------------------------------------------------------------------
 // Down projection.  Grid (S rank splits, column tiles); 8 waves.  A column
-// tile is 128 bytes of each row: 64 bf16 or 128 FP8 columns, NC = 4 or 8 per
-// lane.  Split s owns K-steps [s kps, (s+1) kps) of 32 ranks; wave w takes
+// tile is 128 columns, NC = 8 per lane: 256 bytes of each bf16 row (against
+// 128 with 64 columns, 0.5-0.8 us faster at 4 and 16 tokens) or 128 of each
+// FP8 row.  Split s owns K-steps [s kps, (s+1) kps) of 32 ranks; wave w takes
 // every 8th of them, two in flight.  In a K-step lane l's group g = l / 16
 // owns ranks 8g .. 8g+7 and lane l % 16 owns columns NC (l % 16) .. + NC - 1:
-// it loads those columns of its 8 rows (8 bytes a row) and builds, for each
+// it loads those columns of its 8 rows (16 or 8 bytes a row) and builds, for each
 // column c, the operand of the 8 rows' values in column c (MFMA c: output
 // columns NC j + c, j = 0..15).  The A operand is token l % 16's pieces of s
 // for the same 8 ranks.
 // ------------------------------------------------------------------------
 template <typename TW>
 struct DnRows;
-template <> struct DnRows<uint16_t> {  // bf16: 4 columns a row
-    static constexpr int NC = 4;
+template <> struct DnRows<uint16_t> {  // bf16: 8 columns a row, one 16-byte load
+    static constexpr int NC = 8;
+    using row_t = u32x4;
+    static __device__ __forceinline__ row_t load(const uint16_t *p) { return ld_stream(p); }
     // operands of columns C0 and C0 + 1 (C0 even) of 8 rows
     template <int C0>
-    static __device__ __forceinline__ void operands(const u32x2 (&w)[8], u32x4 &o0, u32x4 &o1)
+    static __device__ __forceinline__ void operands(const row_t (&w)[8], u32x4 &o0, u32x4 &o1)
     {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -372,10 +376,12 @@ template <> struct DnRows<uint16_t> {  // bf16: 4 columns a row
         }
     }
 };
-template <> struct DnRows<uint8_t> {  // FP8: 8 columns a row
+template <> struct DnRows<uint8_t> {  // FP8: 8 columns a row, one 8-byte load
     static constexpr int NC = 8;
+    using row_t = u32x2;
+    static __device__ __forceinline__ row_t load(const uint8_t *p) { return ld_stream8(p); }
     template <int C0>
-    static __device__ __forceinline__ void operands(const u32x2 (&w)[8], u32x4 &o0, u32x4 &o1)
+    static __device__ __forceinline__ void operands(const row_t (&w)[8], u32x4 &o0, u32x4 &o1)
     {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -424,14 +430,14 @@ __global__ __launch_bounds__(512) void dn_batch_kernel(const uint16_t *__restric
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     struct Buf {
-        u32x2 w[8];
+        typename DnRows<TW>::row_t w[8];
         u32x4 a[3];
     };
     auto issue = [&](int n, Buf &b) {  // this wave's n-th K-step
         const int rb = (ks0 + wv + n * kDnWaves) * 32 + 8 * g;
         const int *sl = &ssel[rb - ks0 * 32];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b.w[e] = ld_stream8(wdt + (int64_t)sl[e] * d + col);
+        for (int e = 0; e < 8; ++e) b.w[e] = DnRows<TW>::load(wdt + (int64_t)sl[e] * d + col);
 #pragma unroll
         for (int p = 0; p < 3; ++p)
             b.a[p] = *reinterpret_cast<const u32x4 *>(sp + (int64_t)(p * kBT + li) * KP + rb);
@@ -551,12 +557,12 @@ BatchPlan batch_plan(int d, int k, int B, int fp8)
     p.SK = (d + unit - 1) / unit;
     p.KP = (k + 31) / 32 * 32;
     const int KS = p.KP / 32;
-    const int cols = fp8 ? 128 : 64;
+    const int cols = 128;
     p.n_ct = (d + cols - 1) / cols;
     // rank splits: about 2048 waves, partials (S B d floats, written and
     // read back) under about 1/8 of the down rows' bytes (k d b_w), at least
     // 8 K-steps per split, at most kDnMaxKps
-    int S = (256 + p.n_ct - 1) / p.n_ct;
+    int S = (kDnTargetWgs + p.n_ct - 1) / p.n_ct;
     const int cap = fp8 ? k / (64 * B) : k / (32 * B);
     if (S > cap) S = cap;
     if (S > (KS + 7) / 8) S = (KS + 7) / 8;
@@ -570,8 +576,8 @@ BatchPlan batch_plan(int d, int k, int B, int fp8)
 
 int batch_max_splits(int d, int F)
 {
-    const int n_ct = (d + 127) / 128;  // the FP8 tiling has the fewer column tiles
-    const int a = (256 + n_ct - 1) / n_ct;
+    const int n_ct = (d + 127) / 128;
+    const int a = (kDnTargetWgs + n_ct - 1) / n_ct;
     const int b = ((F + 31) / 32 + kDnMaxKps - 1) / kDnMaxKps;
     return a > b ? a : b;
 }
