@@ -196,8 +196,7 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     w.s_sp = (float *)take(sizeof(float) * B * F);
     w.down_part = (float *)take(sizeof(float) * (size_t)down_s_max * 4 * d);
     if (B > 1) {  // the matrix-core Stage 2 (bf16 activations)
-        const size_t tiles = (size_t)ceil_div(F, 16), chunks = (size_t)ceil_div(d, 1024);
-        w.gu_part = (float *)take(sizeof(float) * tiles * chunks * 512);
+        w.gu_part = (float *)take(sizeof(float) * batch_gu_part_floats((int)d, (int)F));
         w.s_pieces = (uint16_t *)take(sizeof(uint16_t) * 3 * 16 * (size_t)(ceil_div(F, 32) * 32));
         w.bdn_part = (float *)take(sizeof(float) * (size_t)batch_max_splits((int)d, (int)F) * B * d);
     } else {

@@ -109,8 +109,9 @@ hipError_t launch_proxy_batch(const float *xh, int B, int d, int F, const uint8_
                               float *part, float *score, uint32_t *counters, int act, int signal, hipStream_t st);
 // Stage 2 for batches (stage2_batch.hip).
 BatchPlan batch_plan(int d, int k, int B, int fp8);
-int batch_max_splits(int d, int F);  // the largest BatchPlan::S over k <= F
-// gu_part: n_tiles*SK*512 floats; s_pieces: 3*16*KP bf16; dn_part: S*B*d
+int batch_max_splits(int d, int F);         // the largest BatchPlan::S over k <= F
+size_t batch_gu_part_floats(int d, int F);  // the largest gate/up chunk-sum count over k <= F
+// gu_part: (n_tiles - n_full)*SK*512 floats; s_pieces: 3*16*KP bf16; dn_part: S*B*d
 // floats; gu_counters: n_tiles words, dn_counters: n_ct words, zero on entry
 // and left zero.
 hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, int F, const int32_t *sel, int k,

@@ -46,6 +46,7 @@ constexpr int kGuK = kGuWaves * kGuWaveK;    // inputs per gate/up workgroup
 constexpr int kXPitch = kGuK + 8;            // LDS x row, bf16 elements (16-byte pad: no bank conflicts)
 constexpr int kDnWaves = 8;                  // waves per down workgroup
 constexpr int kDnCols = 128;                 // output columns per down workgroup
+constexpr int kGuSplitK = 512;               // inputs per chunk of a split gate/up tile
 constexpr int kDnTargetWgs = 256;           // down workgroups aimed at (column tiles x rank splits)
 constexpr int kDnMaxKps = 64;                // K-steps (32 ranks) per down workgroup, at most
 
@@ -154,7 +155,8 @@ __device__ __forceinline__ void pipeline2(int n, Buf &A, Buf &B, Issue issue, Co
 // is a multiple of the CU count, so the whole tiles take one workgroup slot
 // on every CU and the chunks of the rest fill second slots evenly (269
 // whole tiles on 256 CUs left 13 CUs with two, which ended at 16 us against
-// a median of 9.3).  Wave w takes the 256-input sub-chunks w, w + 4, ... of
+// a median of 9.3; per-workgroup timestamps show each CU's share of the
+// bandwidth, not a workgroup's, setting its pace).  Wave w takes the 256-input sub-chunks w, w + 4, ... of
 // its range, two in flight.
 //
 // The MFMA wants channel l % 16 of the tile in lane l (A) and token l % 16
@@ -548,13 +550,17 @@ BatchPlan batch_plan(int d, int k, int B, int fp8)
 {
     BatchPlan p;
     p.n_tiles = (k + 15) / 16;
-    // whole tiles in multiples of the CU count; the rest in input chunks of
-    // 1024 (one per wave of 4 x 256), which spread evenly over the CUs
+    // whole tiles in multiples of the CU count; the rest in input chunks.
+    // The CUs share the bandwidth about evenly, so the chunks are small:
+    // 512 inputs (16 KB of a bf16 tile) on top of a CU's whole tile.
+    // Measured at 4301 channels: 1024-input chunks (64 KB on 52 CUs) ended
+    // Stage 2 about 1 us later, 256-input ones (16 partials a tile) 0.2 us.
+    // Without whole tiles, chunks of 1024 (one per wave of 4 x 256).
     constexpr int kCUs = 256;
     const int unit = kGuWaves * kGuWaveK;
     p.n_full = p.n_tiles / kCUs * kCUs;
-    p.KW = unit;
-    p.SK = (d + unit - 1) / unit;
+    p.KW = p.n_full > 0 ? kGuSplitK : unit;
+    p.SK = (d + p.KW - 1) / p.KW;
     p.KP = (k + 31) / 32 * 32;
     const int KS = p.KP / 32;
     const int cols = 128;
@@ -572,6 +578,14 @@ BatchPlan batch_plan(int d, int k, int B, int fp8)
     p.kps = (KS + S - 1) / S;
     p.S = (KS + p.kps - 1) / p.kps;
     return p;
+}
+
+size_t batch_gu_part_floats(int d, int F)
+{
+    // (n_tiles - n_full) SK 512 at most: fewer than 256 split tiles, of
+    // at most ceil(d / 256) chunks
+    const int tiles = (F + 15) / 16;
+    return (size_t)(tiles < 255 ? tiles : 255) * (size_t)((d + kGuWaveK - 1) / kGuWaveK) * 512;
 }
 
 int batch_max_splits(int d, int F)
