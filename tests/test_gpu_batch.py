@@ -51,6 +51,15 @@ def test_batch_stage2_given_mask(d, F, B):
     _check(L, B, (1, 15, 17, 33, F // 3 + 1, F), seed=61)
 
 
+@pytest.mark.parametrize("d,F,B", [(1000, 4160, 3), (1536, 4112, 16)])
+def test_batch_stage2_whole_and_chunked_tiles(d, F, B):
+    # k = F gives 260 and 257 gate/up tiles: 256 run whole, the rest in
+    # 512-input chunks (1000 = 512 + 488 inputs, 1536 = 3 x 512) whose sums
+    # meet through a ticket; F // 3 + 1 stays below 256 tiles (chunks of 1024)
+    L = Layer(d, F, 0.02, "bf16", seed=67)
+    _check(L, B, (F, F - 5, F // 3 + 1), seed=67)
+
+
 @pytest.mark.parametrize("B", [4, 16])
 def test_batch_stage2_8b_shape(B):
     # the 4096 x 14336 layer at sparsity 0.7 (k = 4301) and every channel
