@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="fit the sparsity-allocation cost model from measured stage times and test its plans")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the 32-layer chain (RMSNorm + residual between layers) at B = 1 and 8 instead")
     ap.add_argument("--diagnostics", action="store_true",
                     help="mask recall of each selection signal against the exact-state mask, and its time")
     return ap.parse_args()
@@ -118,6 +120,60 @@ def traffic_from_profiles(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def chain_bench(args, torch, P):
+    """End-to-end latency of the 32-layer 4096 x 14336 bf16 FFN stack,
+    h <- h + FFN_l(RMSNorm(h)) per layer through prox_chain_forward, at
+    sparsity 0.7 and keep 0.5, against the same stack dense (sparsity 0).
+    Weights are drawn on the GPU (torch's generator, seed = layer, N(0, 0.02)
+    in binary32 rounded to bf16): 15 GB of layers would take minutes from the
+    host generator, and the values do not change the time (k is fixed).
+    Prints one JSON line per batch size."""
+    wl = synth.WORKLOADS["llama8b_chain32"]
+    d, F, n_layers = wl.d, wl.F, 32
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    layers, proxies = [], []
+    for l in range(n_layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(l)
+        raw = [(torch.randn(shape, generator=g, device=dev) * wl.std).to(torch.bfloat16)
+               for shape in ((F, d), (F, d), (d, F))]
+        w = P.pack_weights(*raw)
+        del raw
+        layers.append(w)
+        proxies.append(P.quantize_proxy(w, wl.mode))
+    torch.cuda.synchronize()
+    print("chain setup %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
+    keep, sp = wl.input_keep, wl.sparsities[0]
+    steps, warmup = max(1, min(args.steps, 40)), max(1, min(args.warmup, 4))
+    for B in wl.batches:
+        x_host = synth.make_x(B, d, wl.dtype, seed=0)
+        h = torch.from_numpy(x_host.view(np.int16)).to(dev).view(torch.bfloat16)
+        res = {}
+        for name, s in (("sparse", sp), ("dense", 0.0)):
+            ws = P.workspace_init(torch.empty(P.chain_workspace_size(d, F, B, wl.mode), dtype=torch.uint8,
+                                              device=dev))
+            for _ in range(warmup):
+                P.chain_forward(h, layers, proxies, keep, s, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                P.chain_forward(h, layers, proxies, keep, s, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = 1000.0 * e0.elapsed_time(e1) / steps
+        print(json.dumps({"metric": "us per 32-layer FFN stack (RMSNorm + residual), 4096x14336 bf16 @70% sparsity",
+                          "value": round(res["sparse"], 1), "unit": "us/stack", "higher_is_better": False,
+                          "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+                          "us_per_layer": round(res["sparse"] / n_layers, 2),
+                          "dense_us_per_stack": round(res["dense"], 1),
+                          "dense_us_per_layer": round(res["dense"] / n_layers, 2),
+                          "config": {"workload": "llama8b_chain32", "layers": n_layers, "batch": B,
+                                     "d_model": d, "d_ff": F, "ffn_sparsity": sp, "input_keep": keep,
+                                     "proxy": wl.mode}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -132,6 +188,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     P.load_library()
+    if args.chain:
+        chain_bench(args, torch, P)
+        return
     wl = synth.WORKLOADS[args.workload]
     d, F, dtype = wl.d, wl.F, wl.dtype
     B = args.batch

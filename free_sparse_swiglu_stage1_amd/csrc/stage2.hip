@@ -549,25 +549,57 @@ __global__ void zero_u32_kernel(uint32_t *p, int n)
     if (i < n) p[i] = 0u;
 }
 
-// RMSNorm with unit gain, fp32 math: out = h / sqrt(mean(h^2) + eps)
+// RMSNorm with unit gain, fp32 math: out = h / sqrt(mean(h^2) + eps).  One
+// workgroup per token.  Every 16-byte load of the row is issued at once
+// through a buffer resource (vectors past d read as zeros, no branch), the
+// row stays in registers for the scaling pass, and each thread's squares are
+// summed in its vector order, then over the wave and the four waves.  (A
+// loop of dependent 2-byte loads took 9.3 us per token row.)
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *h, int d, float eps, T *out)
 {
+    constexpr int V = vec16<T>::N;          // elements per 16-byte vector
+    constexpr int NV = 16384 / V / 256;     // vectors per thread at the largest d
     __shared__ float red[4];
     const int b = blockIdx.x, tid = threadIdx.x;
-    const T *hb = h + (int64_t)b * d;
+    const int nvec = d / V;  // d % 8 == 0
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(h + (int64_t)b * d), (short)0, (int)(sizeof(T) * d), CoherentBuf::kWord3);
+    u32x4 v[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+        v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + 256 * q), 0, 0));
     float ss = 0.0f;
-    for (int i = tid; i < d; i += 256) {
-        const float v = elem<T>::load(hb, i);
-        ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        float f[V];
+        vec16<T>::unpack(v[q], f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) ss = fmaf(f[i], f[i], ss);
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float tot = ((red[0] + red[1]) + red[2]) + red[3];
     const float rms = sqrtf(tot / (float)d + eps);
-    T *ob = out + (int64_t)b * d;
-    for (int i = tid; i < d; i += 256) elem<T>::store(ob, i, elem<T>::load(hb, i) / rms);
+    u32x4 *ob = reinterpret_cast<u32x4 *>(out + (int64_t)b * d);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int e = tid + 256 * q;
+        if (e >= nvec) continue;
+        float f[V];
+        vec16<T>::unpack(v[q], f);
+        u32x4 o;
+        if constexpr (V == 8) {  // bf16, rounded to nearest even
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = (uint32_t)f32_to_bf16(f[2 * i] / rms) | ((uint32_t)f32_to_bf16(f[2 * i + 1] / rms) << 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(f[i] / rms);
+        }
+        ob[e] = o;
+    }
 }
 
 // ------------------------------------------------------------------------
