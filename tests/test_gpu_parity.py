@@ -210,13 +210,19 @@ def test_forward_residual(dtype):
     assert torch.equal(out.view(torch.int16) if dtype == "bf16" else out, ref.view(torch.int16) if dtype == "bf16" else ref)
 
 
-def test_rmsnorm():
-    h = synth.make_x(3, 4096, "bf16", seed=31)
+@pytest.mark.parametrize("B,d,dtype", [(3, 4096, "bf16"), (2, 1000, "bf16"), (1, 16384, "bf16"),
+                                       (2, 520, "f32"), (1, 16384, "f32")])
+def test_rmsnorm(B, d, dtype):
+    # every 16-byte vector of a row loaded at once: rows that end mid-way
+    # through a thread's vectors (d = 1000, 520) and the largest d, where
+    # every thread holds its full share
+    h = synth.make_x(B, d, dtype, seed=31)
     out = P.rmsnorm(to_dev(h), 1e-5)
     torch.cuda.synchronize()
     ref = oracle.rmsnorm(h, 1e-5)
     got = from_dev(out)
-    assert np.abs(got - ref).max() / np.abs(ref).max() < 4e-3  # bf16 output rounding
+    tol = 4e-3 if dtype == "bf16" else 1e-5  # bf16: output rounding; f32: the fp32 bar
+    assert np.abs(got - ref).max() / np.abs(ref).max() < tol
 
 
 def test_workspace_reuse_across_shapes():
