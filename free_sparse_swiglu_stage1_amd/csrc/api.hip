@@ -619,8 +619,25 @@ prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layer
     const size_t need = ffn_bytes + 256 + (size_t)batch * w0.d_model * 4;
     if (workspace_bytes < need) return PROX_ERR_WORKSPACE;
     void *xn = (char *)workspace + align256(ffn_bytes);
+    const int dt = w0.dtype == PROX_F32 ? 0 : 1;
+    if (batch == 1 && fused_supported(1, w0.d_model, w0.d_ff) && k > 0 && k < w0.d_ff) {
+        // one token: the single-token Stage 1 normalizes h itself, bitwise as
+        // the RMSNorm kernel, and hands RMSNorm(h) to Stage 2 in xn; no
+        // separate RMSNorm launch
+        const Workspace ws = layout(w0.d_model, w0.d_ff, 1, proxies[0].mode, workspace);
+        for (int64_t l = 0; l < n_layers; ++l) {
+            const prox_proxy &p = proxies[l];
+            TRY_HIP(launch_stage1_fused(dt, p.mode == PROX_Q_INT4_G128 ? 4 : 8, h, (int)w0.d_model, (int)w0.d_ff,
+                                        (int)k_in, (int)k, (const uint8_t *)p.codes, (const float *)p.scales,
+                                        ws.proxy_part, ws.score, ws.sel, ws.counters, PROX_ACT_SILU, PROX_SIGNAL_S,
+                                        stream, eps, xn));
+            s = run_stage2(xn, 1, &layers[l], ws.sel, k, h, h, nullptr, ws, stream);
+            if (s != PROX_OK) return s;
+        }
+        return PROX_OK;
+    }
     for (int64_t l = 0; l < n_layers; ++l) {
-        TRY_HIP(launch_rmsnorm(w0.dtype == PROX_F32 ? 0 : 1, h, (int)batch, (int)w0.d_model, eps, xn, stream));
+        TRY_HIP(launch_rmsnorm(dt, h, (int)batch, (int)w0.d_model, eps, xn, stream));
         s = forward_impl(xn, batch, &layers[l], &proxies[l], input_keep, ffn_sparsity, h, h, nullptr, workspace,
                          ffn_bytes, stream);
         if (s != PROX_OK) return s;

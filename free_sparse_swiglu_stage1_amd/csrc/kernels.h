@@ -65,9 +65,13 @@ FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
 bool fused_supported(int64_t B, int64_t d, int64_t F);
 // act: the gate activation (0 silu, 1 gelu tanh form); signal: the
 // selection signal (0 |act(g~) u~|, 1 |act(g~)|, 2 |u~|).
+// norm_eps >= 0: x is the residual stream h and every workgroup uses
+// RMSNorm(h) = h / sqrt(mean(h^2) + norm_eps) in x's dtype, bitwise as
+// rmsnorm_kernel computes it; the first workgroup also writes it to xn_out.
 hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
                                const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
-                               uint32_t *counters, int act, int signal, hipStream_t st);
+                               uint32_t *counters, int act, int signal, hipStream_t st, float norm_eps = -1.0f,
+                               void *xn_out = nullptr);
 
 hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
                           int n_counters, hipStream_t st);

@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
                                                            const float *__restrict__ scales, int R, int S,
                                                            int n_cblocks, float *__restrict__ part,
                                                            float *__restrict__ score, int32_t *__restrict__ sel,
-                                                           uint32_t *__restrict__ counters, int act, int signal)
+                                                           uint32_t *__restrict__ counters, int act, int signal,
+                                                           float norm_eps, T *__restrict__ xn_out)
 {
     using Q = Fused<QBITS>;
     constexpr int CPL = Q::CPL;
@@ -108,6 +109,50 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
             const int e = tid + q * kFT;
             const int g = e / (2 * CB), h = (e / CB) & 1, j = min(cb * CB + e % CB, F - 1);
             gs_reg[q] = scales[((int64_t)(i0 / 128 + min(g, ng - 1)) * 2 + h) * F + j];
+        }
+    }
+    if (norm_eps >= 0.0f) {  // x is h: use RMSNorm(h) (uniform branch)
+        // the squares summed as rmsnorm_kernel sums them: threads 0..255,
+        // each over its 16-byte vectors t + 256 q in order (vectors past d
+        // add exact zeros there), then each wave, then the four waves
+        constexpr int VV = vec16<T>::N;
+        constexpr int NQ = (kFusedMaxD / VV + 255) / 256;
+        float ssq = 0.0f;
+        if (tid < 256) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<T *>(x), (short)0, (int)(sizeof(T) * d), CoherentBuf::kWord3);
+            u32x4 hv[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                hv[q] = __builtin_bit_cast(u32x4,
+                                           __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + 256 * q), 0, 0));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                float f[VV];
+                vec16<T>::unpack(hv[q], f);
+#pragma unroll
+                for (int i = 0; i < VV; ++i) ssq = fmaf(f[i], f[i], ssq);
+            }
+        }
+        ssq = wave_sum(ssq);
+        if (lane == 0 && wv < 4) sm.sel.scratch[wv] = __float_as_uint(ssq);  // the bits (a word array)
+        __syncthreads();
+        const float s0 = __uint_as_float(sm.sel.scratch[0]), s1 = __uint_as_float(sm.sel.scratch[1]);
+        const float s2 = __uint_as_float(sm.sel.scratch[2]), s3 = __uint_as_float(sm.sel.scratch[3]);
+        const float rms = sqrtf((((s0 + s1) + s2) + s3) / (float)d + norm_eps);
+        __syncthreads();
+        auto norm = [&](float v) {  // rounded to x's dtype, as rmsnorm_kernel stores it
+            const float y = v / rms;
+            return sizeof(T) == 2 ? __uint_as_float((uint32_t)f32_to_bf16(y) << 16) : y;
+        };
+#pragma unroll
+        for (int r = 0; r < KX; ++r) xv[r] = norm(xv[r]);
+#pragma unroll
+        for (int q = 0; q < XR; ++q) xr[q] = norm(xr[q]);
+        if (xn_out && blockIdx.x == 0 && blockIdx.y == 0) {
+#pragma unroll
+            for (int r = 0; r < KX; ++r)
+                if (slot_index<KX>(r) < d) elem<T>::store(xn_out, slot_index<KX>(r), xv[r]);
         }
     }
     uint32_t key[KX];
@@ -329,7 +374,7 @@ bool fused_supported(int64_t B, int64_t d, int64_t F) { return B == 1 && d <= kF
 
 hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
                                const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
-                               uint32_t *counters, int act, int signal, hipStream_t st)
+                               uint32_t *counters, int act, int signal, hipStream_t st, float norm_eps, void *xn_out)
 {
     if (!fused_supported(1, d, F)) return hipErrorInvalidValue;
     const FusedPlan pl = fused_plan(qbits, d, F);
@@ -339,7 +384,7 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
 #define L1(T, Q, KXV, KFV)                                                                               \
     stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k, codes, scales, \
                                                              pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
-                                                             counters, act, signal)
+                                                             counters, act, signal, norm_eps, (T *)xn_out)
 #define L2(T, Q)                                       \
     do {                                               \
         if (kx <= 2 && kf <= 16) L1(T, Q, 2, 16);      \
