@@ -220,9 +220,12 @@ prox_status hip_status(hipError_t e) { return e == hipSuccess ? PROX_OK : PROX_E
 hipError_t mark(hipEvent_t *ev, int i, hipStream_t st) { return ev ? hipEventRecord(ev[i], st) : hipSuccess; }
 
 // Stage 1 into `sel` (k entries), scores into `score`.
+// norm_eps >= 0: x is h; Stage 1 uses RMSNorm(h) and writes it to xn (see
+// launch_stage1_fused and launch_xselect).
 prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const prox_proxy *p, int64_t k_in,
                        int64_t k, int32_t *sel, float *score, const Workspace &ws, hipStream_t st,
-                       hipEvent_t *ev = nullptr, const Opts &o = Opts())
+                       hipEvent_t *ev = nullptr, const Opts &o = Opts(), float norm_eps = -1.0f,
+                       void *xn = nullptr)
 {
     const int64_t d = w->d_model, F = w->d_ff;
     const int dt = w->dtype == PROX_F32 ? 0 : 1;
@@ -230,14 +233,14 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
         TRY_HIP(mark(ev, 0, st));
         TRY_HIP(launch_stage1_fused(dt, p->mode == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
                                     (const uint8_t *)p->codes, (const float *)p->scales, ws.proxy_part, score, sel,
-                                    ws.counters, o.act, o.signal, st));
+                                    ws.counters, o.act, o.signal, st, norm_eps, xn));
         TRY_HIP(mark(ev, 1, st));
         return hip_status(mark(ev, 2, st));
     }
     const ProxyPlan pp = proxy_plan(d, F, B, p->mode);
     TRY_HIP(mark(ev, 0, st));
     TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
-                           kTicketWords, st));
+                           kTicketWords, st, norm_eps, xn));
     TRY_HIP(mark(ev, 1, st));
     // bf16 batches above 4 tokens, int8 codes: the matrix cores (at 4 tokens
     // the vector-ALU kernel is faster, 32.6 against 35.3 us at 4096 x 14336)
@@ -620,18 +623,25 @@ prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layer
     if (workspace_bytes < need) return PROX_ERR_WORKSPACE;
     void *xn = (char *)workspace + align256(ffn_bytes);
     const int dt = w0.dtype == PROX_F32 ? 0 : 1;
-    if (batch == 1 && fused_supported(1, w0.d_model, w0.d_ff) && k > 0 && k < w0.d_ff) {
-        // one token: the single-token Stage 1 normalizes h itself, bitwise as
-        // the RMSNorm kernel, and hands RMSNorm(h) to Stage 2 in xn; no
-        // separate RMSNorm launch
-        const Workspace ws = layout(w0.d_model, w0.d_ff, 1, proxies[0].mode, workspace);
+    if (k > 0 && k < w0.d_ff) {
+        // Stage 1's first kernel (the single-token kernel, or the input
+        // selection of a batch) normalizes h itself, bitwise as the RMSNorm
+        // kernel, and hands RMSNorm(h) to Stage 2 in xn: no RMSNorm launch
+        const Workspace ws = layout(w0.d_model, w0.d_ff, batch, proxies[0].mode, workspace);
+        const bool fused = batch == 1 && fused_supported(1, w0.d_model, w0.d_ff);
         for (int64_t l = 0; l < n_layers; ++l) {
             const prox_proxy &p = proxies[l];
-            TRY_HIP(launch_stage1_fused(dt, p.mode == PROX_Q_INT4_G128 ? 4 : 8, h, (int)w0.d_model, (int)w0.d_ff,
-                                        (int)k_in, (int)k, (const uint8_t *)p.codes, (const float *)p.scales,
-                                        ws.proxy_part, ws.score, ws.sel, ws.counters, PROX_ACT_SILU, PROX_SIGNAL_S,
-                                        stream, eps, xn));
-            s = run_stage2(xn, 1, &layers[l], ws.sel, k, h, h, nullptr, ws, stream);
+            if (fused) {
+                TRY_HIP(launch_stage1_fused(dt, p.mode == PROX_Q_INT4_G128 ? 4 : 8, h, (int)w0.d_model,
+                                            (int)w0.d_ff, (int)k_in, (int)k, (const uint8_t *)p.codes,
+                                            (const float *)p.scales, ws.proxy_part, ws.score, ws.sel, ws.counters,
+                                            PROX_ACT_SILU, PROX_SIGNAL_S, stream, eps, xn));
+            } else {
+                s = run_stage1(h, batch, &layers[l], &p, k_in, k, ws.sel, ws.score, ws, stream, nullptr, Opts(), eps,
+                               xn);
+                if (s != PROX_OK) return s;
+            }
+            s = run_stage2(xn, batch, &layers[l], ws.sel, k, h, h, nullptr, ws, stream);
             if (s != PROX_OK) return s;
         }
         return PROX_OK;

@@ -74,7 +74,8 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
                                void *xn_out = nullptr);
 
 hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
-                          int n_counters, hipStream_t st);
+                          int n_counters, hipStream_t st, float norm_eps = -1.0f,
+                          void *xn_out = nullptr);
 hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
                         const float *scales, float *part, float *score, uint32_t *counters, int act, int signal,
                         hipStream_t st);

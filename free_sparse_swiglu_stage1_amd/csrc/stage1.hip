@@ -19,7 +19,7 @@ namespace prox {
 template <typename T, int KPT>
 __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, int d, int k_in,
                                                        float *__restrict__ xh, uint32_t *__restrict__ counters,
-                                                       int n_counters)
+                                                       int n_counters, float norm_eps, T *__restrict__ xn_out)
 {
     __shared__ SelectSmem<16384> sm;
     const int b = blockIdx.x;
@@ -32,6 +32,45 @@ __global__ __launch_bounds__(1024) void xselect_kernel(const T *__restrict__ x, 
     for (int r = 0; r < KPT; ++r) {  // all loads issued before any use
         const int i = slot_index<KPT>(r);
         v[r] = elem<T>::load(xb, i < d ? i : d - 1);
+    }
+    if (norm_eps >= 0.0f) {  // x is h: select on RMSNorm(h) and write it to xn_out
+        // the squares summed as rmsnorm_kernel sums them: threads 0..255,
+        // each over its 16-byte vectors t + 256 q in order (vectors past d
+        // add exact zeros there), then each wave, then the four waves
+        constexpr int VV = vec16<T>::N;
+        constexpr int NQ = 16384 / VV / 256;
+        const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+        float ssq = 0.0f;
+        if (tid < 256) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<T *>(xb), (short)0, (int)(sizeof(T) * d), CoherentBuf::kWord3);
+            u32x4 hv[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                hv[q] = __builtin_bit_cast(u32x4,
+                                           __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + 256 * q), 0, 0));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                float f[VV];
+                vec16<T>::unpack(hv[q], f);
+#pragma unroll
+                for (int i = 0; i < VV; ++i) ssq = fmaf(f[i], f[i], ssq);
+            }
+        }
+        ssq = wave_sum(ssq);
+        if (lane == 0 && wv < 4) sm.scratch[wv] = __float_as_uint(ssq);  // the bits (a word array)
+        __syncthreads();
+        const float s0 = __uint_as_float(sm.scratch[0]), s1 = __uint_as_float(sm.scratch[1]);
+        const float s2 = __uint_as_float(sm.scratch[2]), s3 = __uint_as_float(sm.scratch[3]);
+        const float rms = sqrtf((((s0 + s1) + s2) + s3) / (float)d + norm_eps);
+        __syncthreads();
+        T *xo = xn_out + (int64_t)b * d;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {  // rounded to x's dtype, as rmsnorm_kernel stores it
+            const float y = v[r] / rms;
+            v[r] = sizeof(T) == 2 ? __uint_as_float((uint32_t)f32_to_bf16(y) << 16) : y;
+            if (slot_index<KPT>(r) < d) elem<T>::store(xo, slot_index<KPT>(r), v[r]);
+        }
     }
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
@@ -326,22 +365,25 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ sc
 // ------------------------------------------------------------------------
 template <typename T>
 static hipError_t launch_xselect_t(const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
-                                   int n_counters, hipStream_t st)
+                                   int n_counters, hipStream_t st, float norm_eps, void *xn_out)
 {
     const int kpt = (d + 1023) / 1024;
     const T *xp = (const T *)x;
 #define XS(K) \
-    if (kpt <= K) { xselect_kernel<T, K><<<B, 1024, 0, st>>>(xp, d, k_in, xh, counters, n_counters); return hipGetLastError(); }
+    if (kpt <= K) {                                                                                             \
+        xselect_kernel<T, K><<<B, 1024, 0, st>>>(xp, d, k_in, xh, counters, n_counters, norm_eps, (T *)xn_out); \
+        return hipGetLastError();                                                                               \
+    }
     XS(1) XS(2) XS(4) XS(8) XS(16)
 #undef XS
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_xselect(int dtype, const void *x, int B, int d, int k_in, float *xh, uint32_t *counters,
-                          int n_counters, hipStream_t st)
+                          int n_counters, hipStream_t st, float norm_eps, void *xn_out)
 {
-    return dtype == 0 ? launch_xselect_t<float>(x, B, d, k_in, xh, counters, n_counters, st)
-                      : launch_xselect_t<uint16_t>(x, B, d, k_in, xh, counters, n_counters, st);
+    return dtype == 0 ? launch_xselect_t<float>(x, B, d, k_in, xh, counters, n_counters, st, norm_eps, xn_out)
+                      : launch_xselect_t<uint16_t>(x, B, d, k_in, xh, counters, n_counters, st, norm_eps, xn_out);
 }
 
 hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int F, const uint8_t *codes,
