@@ -323,7 +323,9 @@ prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d_model, prox_dty
  * h [B][d] device (dtype of the layers); layers[l], proxies[l] host arrays of
  * descriptors with identical shapes and dtype.  The workspace must hold
  * prox_workspace_size(d, F, B, mode) + 256 + B*d*4 bytes (the normalized
- * input is staged there). */
+ * input is staged there).  Each layer's result equals, bitwise, prox_rmsnorm
+ * of h followed by prox_ffn_forward of that with residual h; with a sparse
+ * mask Stage 1 computes the norm itself instead of a separate launch. */
 prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layers,
                                const prox_proxy *proxies, int64_t n_layers, float eps,
                                float input_keep, float ffn_sparsity, void *workspace,
