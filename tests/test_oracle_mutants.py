@@ -33,6 +33,9 @@ MUTANTS = [
     ("down weight transposed", "(double)wd[m * F + sel[t]]", "(double)wd[(sel[t] * d + m) % (d * F)]"),
     ("one input too few kept", "for (int64_t t = 0; t < k_in; ++t)", "for (int64_t t = 0; t + 1 < k_in; ++t)"),
     ("rmsnorm without eps", "sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d)"),
+    ("rmsnorm sum not reset per token", "for (int64_t b = 0; b < B; ++b) {\n        double ss = 0.0;",
+     "double ss = 0.0;\n    for (int64_t b = 0; b < B; ++b) {"),
+    ("rmsnorm squares of token 0 for all", "ss += h[b * d + i] * h[b * d + i];", "ss += h[i] * h[i];"),
     ("silu missing z", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     ("e4m3 exponent bias 8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     ("e4m3 subnormals 2^-10", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),

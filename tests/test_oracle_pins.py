@@ -556,6 +556,25 @@ def test_rmsnorm_closed_forms(oracle):
     np.testing.assert_allclose(r[0], np.array([3.0, 4.0]) / math.sqrt(12.5 + 1e-5), rtol=1e-15)
 
 
+def test_rmsnorm_batch_rows_independent(oracle):
+    """Every token is normalized by its own mean square: rows of different
+    closed forms in one batch (a constant row c -> c / sqrt(c^2 + eps), the
+    [3, 4] row -> [3, 4] / sqrt(12.5 + eps), a zero row -> 0, a row whose
+    entries cancel in a plain sum), each as it is on its own."""
+    eps = 1e-5
+    h = np.array([[7.0, 7.0], [3.0, 4.0], [0.0, 0.0], [-6.0, 6.0], [0.5, -0.25]], dtype=np.float32)
+    r = oracle.rmsnorm(h, eps)
+    np.testing.assert_allclose(r[0], 7.0 / math.sqrt(49.0 + eps), rtol=1e-15)
+    np.testing.assert_allclose(r[1], np.array([3.0, 4.0]) / math.sqrt(12.5 + eps), rtol=1e-15)
+    assert np.all(r[2] == 0.0)
+    np.testing.assert_allclose(r[3], np.array([-6.0, 6.0]) / math.sqrt(36.0 + eps), rtol=1e-15)
+    np.testing.assert_allclose(r[4], np.array([0.5, -0.25]) / math.sqrt(0.15625 + eps), rtol=1e-15)
+    # and each row equals the row normalized alone, whatever its neighbours
+    for b in range(h.shape[0]):
+        np.testing.assert_array_equal(oracle.rmsnorm(h[b:b + 1], eps)[0], r[b])
+        np.testing.assert_array_equal(oracle.rmsnorm(h[::-1], eps)[h.shape[0] - 1 - b], r[b])
+
+
 # ------------------------------------------------------- acceptance rule
 
 def test_mask_admissible_rule(oracle):
