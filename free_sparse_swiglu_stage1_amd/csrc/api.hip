@@ -4,6 +4,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/prox.h"
 #include "kernels.h"
@@ -16,18 +17,21 @@ constexpr int kMaxBatch = 16;
 constexpr int kMaxBatchInt4 = 4;
 // The workspace starts with counters that must be zero between calls:
 // [0,511) proxy channel blocks, 511 the single-token Stage 1's score ticket,
-// [512,1023) down slices, 1023 a wait-timeout flag, [1024,1535) the
-// single-token Stage 2's finished slice tails, then from 4096 the
-// single-token Stage 2's per-split lines (64 pages of 4 KB).  Each is reset
-// by the last workgroup to use it.
+// [512,1023) down slices, [1024,1535) the single-token Stage 2's finished
+// slice tails, [1536,2047) its slice-tail claims, 2047 the count of bounded
+// waits that gave up (never reset by a call), then from 4096 the
+// single-token Stage 2's per-split lines (64 pages of 4 KB).  Each other word
+// is reset by the last workgroup to use it.
 constexpr int kCounters = kS2SyncBase + kS2SyncWords;
 constexpr int kZeroWords = kCounters;
-// The ticket words and the timeout flag: the batched Stage 1 clears them
+// The channel-block and slice ticket words: the batched Stage 1 clears them
 // again on entry, inside its first kernel.
-constexpr int kTicketWords = kS2TimeoutSlot + 1;
+constexpr int kTicketWords = kDownSliceEnd;
 constexpr int kTargetProxyBlocks = 1024;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+prox_status hip_status(hipError_t e) { return e == hipSuccess ? PROX_OK : PROX_ERR_HIP; }
 
 bool bad_ptr(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) != 0; }
 bool bad_ptr_opt(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
@@ -70,6 +74,7 @@ prox_status check_weights(const prox_weights *w)
 struct Opts {
     int act = PROX_ACT_SILU;
     int signal = PROX_SIGNAL_S;
+    uint64_t spin_ticks = 0;  // 0: the kernels' default bound
 };
 
 prox_status check_options(const prox_options *o, Opts *out)
@@ -77,8 +82,10 @@ prox_status check_options(const prox_options *o, Opts *out)
     if (!o) return PROX_OK;
     if (o->activation != PROX_ACT_SILU && o->activation != PROX_ACT_GELU_TANH) return PROX_ERR_UNSUPPORTED;
     if (o->signal < PROX_SIGNAL_S || o->signal > PROX_SIGNAL_EXACT_S) return PROX_ERR_UNSUPPORTED;
+    if (o->wait_limit_ticks < 0) return PROX_ERR_INVALID_ARG;
     out->act = o->activation;
     out->signal = o->signal;
+    out->spin_ticks = (uint64_t)o->wait_limit_ticks;
     return PROX_OK;
 }
 
@@ -208,8 +215,6 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     return w;
 }
 
-prox_status hip_status(hipError_t e) { return e == hipSuccess ? PROX_OK : PROX_ERR_HIP; }
-
 #define TRY_HIP(expr)                                           \
     do {                                                        \
         hipError_t e_ = (expr);                                 \
@@ -271,7 +276,7 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
     }
     if (B == 1) {  // one launch: the down projection starts while gate/up drains
         TRY_HIP(launch_stage2_fused(dt, sw, x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part, residual,
-                                    out, ws.counters, iota_out, st));
+                                    out, ws.counters, iota_out, st, o.spin_ticks));
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
@@ -367,7 +372,7 @@ const char *prox_status_string(int status)
     }
 }
 
-const char *prox_version(void) { return "prox-gfx950 0.1"; }
+const char *prox_version(void) { return "prox-gfx950 0.2"; }
 
 prox_status prox_counts(int64_t d, int64_t F, float keep, float sp, int64_t *k_in, int64_t *k)
 {
@@ -490,6 +495,27 @@ prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStre
     return hip_status(launch_zero_u32((uint32_t *)workspace, kZeroWords, stream));
 }
 
+prox_status prox_workspace_check(const void *workspace, size_t workspace_bytes, uint32_t *fallbacks,
+                                 hipStream_t stream)
+{
+    if (bad_ptr(workspace) || !fallbacks) return PROX_ERR_INVALID_ARG;
+    if (workspace_bytes < sizeof(uint32_t) * kZeroWords) return PROX_ERR_WORKSPACE;
+    uint32_t *h = (uint32_t *)malloc(sizeof(uint32_t) * kZeroWords);  // host memory
+    if (!h) return PROX_ERR_HIP;
+    hipError_t e = hipMemcpyAsync(h, workspace, sizeof(uint32_t) * kZeroWords, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        free(h);
+        return PROX_ERR_HIP;
+    }
+    bool clean = true;
+    for (int i = 0; i < kZeroWords; ++i)
+        if (i != kFallbackSlot && h[i] != 0u) clean = false;
+    *fallbacks = h[kFallbackSlot];
+    free(h);
+    return clean ? PROX_OK : PROX_ERR_WORKSPACE;
+}
+
 prox_status prox_ffn_forward(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
                              float input_keep, float ffn_sparsity, void *out, int32_t *sel_idx_out,
                              void *workspace, size_t workspace_bytes, hipStream_t stream)
@@ -589,7 +615,9 @@ prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d, prox_dtype dty
                          hipStream_t stream)
 {
     if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
-    if (batch < 1 || batch > 4096 || d < 1 || d > 65536 || isnan(eps) || eps < 0.0f) return PROX_ERR_INVALID_ARG;
+    if (batch < 1 || batch > 4096 || isnan(eps) || eps < 0.0f) return PROX_ERR_INVALID_ARG;
+    // the kernel holds a row in 16-byte vectors, at most 16384 elements
+    if (d < 8 || d > 16384 || d % 8 != 0) return PROX_ERR_UNSUPPORTED;
     if (bad_ptr(h) || bad_ptr(out)) return PROX_ERR_INVALID_ARG;
     return hip_status(launch_rmsnorm(dtype == PROX_F32 ? 0 : 1, h, (int)batch, (int)d, eps, out, stream));
 }

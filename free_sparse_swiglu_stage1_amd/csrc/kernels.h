@@ -124,16 +124,21 @@ hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, 
                                const void *residual, void *out, uint32_t *gu_counters, uint32_t *dn_counters,
                                int32_t *iota_out, hipStream_t st);
 // Stage 2 for one token in one launch (stage2.hip).  Counter slots:
-// [kDownSliceBase, +511) slice tickets, [kDownPassBase, +511) slice-tail
-// counts, kS2TimeoutSlot a wait timeout, and
-// from kS2SyncBase one 128-byte line per split (its readiness count, then its
-// count of down workgroups past the wait).  Split s sits in 4 KB page s % 64,
-// line s / 64: the lines being polled at one time are 4 KB apart, so the
-// polls spread over the memory channels instead of queueing on one (one
-// packed run of counters slowed every gate/up row on that channel about 3x).
+// [kDownSliceBase, kDownSliceEnd) slice tickets, [kDownPassBase, +511)
+// slice-tail counts, [kDownClaimBase, +511) slice-tail group claims, and from
+// kS2SyncBase one 128-byte line per split holding its arrival count (gate/up
+// workgroups add 1, down workgroups 1 << 16 once past their wait).  Split s
+// sits in 4 KB page s % 64, line s / 64: the lines being polled at one time
+// are 4 KB apart, so the polls spread over the memory channels instead of
+// queueing on one (one packed run of counters slowed every gate/up row on
+// that channel about 3x).  kFallbackSlot counts bounded waits that gave up
+// (each then completed its work without the awaited data); unlike the others
+// it is not reset by the kernels, only by a zero fill of the workspace.
 constexpr int kDownSliceBase = 512;
+constexpr int kDownSliceEnd = 1023;
 constexpr int kDownPassBase = 1024;
-constexpr int kS2TimeoutSlot = 1023;
+constexpr int kDownClaimBase = 1536;
+constexpr int kFallbackSlot = 2047;
 constexpr int kS2SyncBase = 4096;
 constexpr int kS2SyncPages = 64;
 constexpr int kS2PageWords = 1024;
@@ -144,10 +149,14 @@ __host__ __device__ constexpr int s2_sync_line(int s)
 {
     return kS2SyncBase + (s % kS2SyncPages) * kS2PageWords + (s / kS2SyncPages) * kS2LineWords;
 }
+// Bounded cross-workgroup waits give up after spin_ticks of the 100 MHz
+// real-time counter (0: kDefaultSpinTicks, half a second).
+constexpr uint64_t kDefaultSpinTicks = 50000000ull;
 hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int d, int F, const int32_t *sel, int k,
                                float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
-                               int32_t *iota_out, hipStream_t st);
+                               int32_t *iota_out, hipStream_t st, uint64_t spin_ticks = 0);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
+
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
 
 hipError_t launch_pack(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,

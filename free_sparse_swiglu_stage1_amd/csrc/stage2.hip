@@ -263,35 +263,46 @@ __global__ __launch_bounds__(256) void gateup_kernel(const T *__restrict__ x, in
 // order -- adds the residual if any, rounds and stores.
 // ------------------------------------------------------------------------
 
-constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s of the 100 MHz real-time counter
-
-// Waits (one thread) until *ctr >= target; false after kSpinTicks.
-__device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target)
+// Waits (one thread) until (*ctr & mask) >= target; false once `ticks` of
+// the 100 MHz real-time counter have passed without it.
+__device__ __forceinline__ bool spin_wait_geq(uint32_t *ctr, uint32_t target, uint64_t ticks,
+                                              uint32_t mask = 0xFFFFFFFFu)
 {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while ((__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & mask) < target) {
         __builtin_amdgcn_s_sleep(8);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
     }
     return true;
+}
+
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The end of a down-projection workgroup: its waves' accumulators are added
 // in LDS in wave order into this split's partial (coherent 64-bit stores),
 // then it takes a ticket on its slice.  The last TG arrivals (TG when the
-// slice has at least TG splits, else 1) each finish one of TG column groups
-// of the slice: the earlier ones first wait until every split has arrived,
-// then each adds its columns' partials -- interleaved groups of splits in
-// parallel, each group in split order, then the groups in order --
-// multiplies by the output row's FP8 scale if any (dsc), adds the residual if
-// any, rounds and stores.  The last of them to finish resets the slice's
-// counters (slice_counter: arrivals; pass_counter: finished tails, TG > 1).
-// A wait that outlasts kSpinTicks sets *timeout_flag and goes on.
+// slice has at least TG splits, else 1) share the slice's tail, one of TG
+// column groups each: a group adds its columns' partials -- interleaved
+// groups of splits in parallel, each group in split order, then the groups
+// in order -- multiplies by the output row's FP8 scale if any (dsc), adds the
+// residual if any, rounds and stores.  The last arrival knows every partial
+// is written and finishes group TG-1 at once; an earlier one first waits
+// (bounded by spin_ticks) until every split has arrived, then claims its
+// group with one bit of *claim.  After its own group the last arrival claims
+// every group still unclaimed and finishes it too, so a wait that gives up
+// (counted in *fallback) costs time, never a missing or wrong output.  The
+// last of the tail workgroups to finish resets the slice's words
+// (slice_counter: arrivals; pass_counter: finished tails; claim).
+// s_flags: two ints of LDS.
 template <typename T, int V, int NB, int NW, int TG>
-__device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&red)[NW][NB][64 * V], int *s_last,
+__device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&red)[NW][NB][64 * V], int *s_flags,
                                             int sl, int s, int B, int d, int S, float *__restrict__ part,
                                             const float *__restrict__ dsc, const T *residual, T *out,
-                                            uint32_t *slice_counter, uint32_t *pass_counter, uint32_t *timeout_flag)
+                                            uint32_t *slice_counter, uint32_t *pass_counter, uint32_t *claim,
+                                            uint32_t *fallback, uint64_t spin_ticks)
 {
     constexpr int NT = 64 * NW;
     constexpr int COLS = 64 * V;
@@ -315,66 +326,94 @@ __device__ __forceinline__ void down_finish(const float (&acc)[NB][V], float (&r
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
     __syncthreads();
-    if (tid == 0)
-        *s_last = (int)__hip_atomic_fetch_add(slice_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_flags[0] = (int)atomic_add_agent(slice_counter, 1u);
     __syncthreads();
-    const int t = uniform(*s_last);
+    const int t = uniform(s_flags[0]);
     const int ng = (TG > 1 && S >= TG) ? TG : 1;  // column groups of the tail
     if (t < S - ng) return;
-    const int g = t - (S - ng);  // this workgroup's group
-    if (ng > 1 && t != S - 1) {  // not the last arrival: wait for the others
-        if (tid == 0 && !spin_wait_geq(slice_counter, (uint32_t)S))
-            __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-    }
-    // thread t: column pair t % PAIRS of this group, of the splits grp,
-    // grp + GROUPS, grp + 2*GROUPS, ... (grp = t / PAIRS); every load is one
-    // this thread needs, issued before any is added (wave-uniform predicate)
+
+    // one column group of the tail: thread t takes column pair t % PAIRS of
+    // the group, of the splits grp, grp + GROUPS, grp + 2*GROUPS, ... (grp =
+    // t / PAIRS); every load is one this thread needs, issued before any is
+    // added (wave-uniform predicate)
     const int CG = COLS / ng, PAIRS = CG / 2, GROUPS = NT / PAIRS;
     constexpr int QMAX = 36;  // splits per thread the loads cover in one batch
     const int pair = tid % PAIRS, grp = tid / PAIRS;
-    const int c0 = sl * COLS + g * CG;  // the group's first column
-    const int col0 = c0 + pair * 2;
     const int nq = (S - grp + GROUPS - 1) / GROUPS;  // this thread's splits
     float *gsum = &red[0][0][0];                     // [GROUPS][NB][CG]
-    __syncthreads();
     const CoherentBuf pbuf(part, (uint32_t)(sizeof(float) * S * B * d));
-    for (int b = 0; b < NB; ++b) {
-        float y0 = 0.0f, y1 = 0.0f;
-        if (b < B && col0 < d) {
-            for (int q0 = 0; q0 < nq; q0 += QMAX) {
-                float v0[QMAX], v1[QMAX];
+    auto tail_group = [&](int g) {
+        const int c0 = sl * COLS + g * CG;  // the group's first column
+        const int col0 = c0 + pair * 2;
+        __syncthreads();  // gsum free (red read, or a previous group's sums used)
+        for (int b = 0; b < NB; ++b) {
+            float y0 = 0.0f, y1 = 0.0f;
+            if (b < B && col0 < d) {
+                for (int q0 = 0; q0 < nq; q0 += QMAX) {
+                    float v0[QMAX], v1[QMAX];
 #pragma unroll
-                for (int i = 0; i < QMAX; ++i) {  // past this thread's splits: beyond the buffer, reads 0
-                    const uint32_t q = (uint32_t)min(grp + (q0 + i) * GROUPS, S);
-                    pbuf.load2((uint32_t)(sizeof(float) * ((q * B + b) * d + col0)), v0[i], v1[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < QMAX; ++i)
-                    if (q0 + i < nq) {
-                        y0 += v0[i];
-                        y1 += v1[i];
+                    for (int i = 0; i < QMAX; ++i) {  // past this thread's splits: beyond the buffer, reads 0
+                        const uint32_t q = (uint32_t)min(grp + (q0 + i) * GROUPS, S);
+                        pbuf.load2((uint32_t)(sizeof(float) * ((q * B + b) * d + col0)), v0[i], v1[i]);
                     }
+#pragma unroll
+                    for (int i = 0; i < QMAX; ++i)
+                        if (q0 + i < nq) {
+                            y0 += v0[i];
+                            y1 += v1[i];
+                        }
+                }
             }
+            gsum[(grp * NB + b) * CG + pair * 2] = y0;
+            gsum[(grp * NB + b) * CG + pair * 2 + 1] = y1;
         }
-        gsum[(grp * NB + b) * CG + pair * 2] = y0;
-        gsum[(grp * NB + b) * CG + pair * 2 + 1] = y1;
+        __syncthreads();
+        for (int e = tid; e < B * CG; e += NT) {
+            const int b = e / CG, ci = e % CG, col = c0 + ci;
+            if (col >= d || b >= NB) continue;
+            float y = gsum[b * CG + ci];
+            for (int gg = 1; gg < GROUPS; ++gg) y += gsum[(gg * NB + b) * CG + ci];
+            if (dsc) y *= dsc[col];
+            if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
+            elem<T>::store(out, (int64_t)b * d + col, y);
+        }
+    };
+    // claims group g for this workgroup (one thread asks, all get the answer)
+    auto claim_group = [&](int g) {
+        if (tid == 0)
+            s_flags[1] = (__hip_atomic_fetch_or(claim, 1u << g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                          (1u << g)) == 0u;
+        __syncthreads();
+        const bool mine = uniform(s_flags[1]) != 0;
+        __syncthreads();  // s_flags[1] read by every thread before its next write
+        return mine;
+    };
+
+    if (t == S - 1) {  // the last arrival: every partial is in place
+        tail_group(ng - 1);
+        for (int g = 0; g < ng - 1; ++g)
+            if (claim_group(g)) tail_group(g);
+    } else {  // an earlier tail workgroup: wait for the last, then claim its group
+        const int g = t - (S - ng);
+        if (tid == 0) {
+            const bool ok = spin_wait_geq(slice_counter, (uint32_t)S, spin_ticks);
+            if (!ok) atomic_add_agent(fallback, 1u);
+            s_flags[1] = ok ? 1 : 0;
+        }
+        __syncthreads();
+        const bool arrived = uniform(s_flags[1]) != 0;
+        __syncthreads();
+        if (arrived && claim_group(g)) tail_group(g);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int e = tid; e < B * CG; e += NT) {
-        const int b = e / CG, ci = e % CG, col = c0 + ci;
-        if (col >= d || b >= NB) continue;
-        float y = gsum[b * CG + ci];
-        for (int gg = 1; gg < GROUPS; ++gg) y += gsum[(gg * NB + b) * CG + ci];
-        if (dsc) y *= dsc[col];
-        if (residual) y += elem<T>::load(residual, (int64_t)b * d + col);
-        elem<T>::store(out, (int64_t)b * d + col, y);
-    }
-    if (tid == 0) {  // the slice's counters back to zero once no one reads them
-        if (ng == 1 ||
-            __hip_atomic_fetch_add(pass_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)ng - 1) {
+    if (tid == 0) {  // the slice's words back to zero once no tail workgroup touches them
+        if (ng == 1 || atomic_add_agent(pass_counter, 1u) == (uint32_t)ng - 1) {
             __hip_atomic_store(slice_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (ng > 1) __hip_atomic_store(pass_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (ng > 1) {
+                __hip_atomic_store(pass_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -390,7 +429,7 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
     constexpr int COLS = 64 * V;
     constexpr int U = kDownRowsPerWave;
     __shared__ float red[NW][NB][COLS];
-    __shared__ int s_last;
+    __shared__ int s_flags[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int sl = blockIdx.x, s = blockIdx.y;
     const int c = sl * COLS + lane * V;
@@ -432,8 +471,8 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
         }
     }
 
-    down_finish<T, V, NB, NW, 1>(acc, red, &s_last, sl, s, B, d, S, part, dsc, residual, out, &counters[sl], nullptr,
-                                 nullptr);
+    down_finish<T, V, NB, NW, 1>(acc, red, s_flags, sl, s, B, d, S, part, dsc, residual, out, &counters[sl], nullptr,
+                                 nullptr, nullptr, 0);
 }
 
 // ------------------------------------------------------------------------
@@ -441,66 +480,80 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(const float *__restrict__
 // overlaps the gate/up tail instead of following a kernel boundary.
 //
 // Workgroups [0, n_gu) are gate/up workgroups (gateup_block, s stored
-// device-coherently) that count themselves done in their split's readiness
-// counter (its own 128-byte line, s2_sync_line); a split is
-// 64 ranks, i.e. 16 gate/up workgroups.  Workgroups [n_gu, n_gu + n_down) are
-// down workgroups (slice, split): each waits until the 16 gate/up workgroups
-// of its split are done, then streams its 64 rows (4 waves x 16 rows, all in
-// flight) and ends as down_kernel does.  Waiting before loading keeps the
-// down rows out of the memory queue while the gate/up rows drain.
+// device-coherently) that count themselves done in their split's arrival
+// word (its own 128-byte line, s2_sync_line); a split is 64 ranks, i.e. 16
+// gate/up workgroups.  Workgroups [n_gu, n_gu + n_down) are down workgroups
+// (slice, split): each waits until the gate/up workgroups of its split are
+// done, then streams its 64 rows (4 waves x 16 rows, all in flight) and ends
+// as down_kernel does.  Waiting before loading keeps the down rows out of the
+// memory queue while the gate/up rows drain.
 //
 // Workgroups are dispatched in index order on every XCD, so every gate/up
 // workgroup has been dispatched before any down workgroup waits, and gate/up
-// workgroups wait for nothing.  The wait is bounded in time all the same (a
-// timeout sets counters[kS2TimeoutSlot] and the workgroup goes on); the last
-// down workgroup of a split to pass the wait resets its counters.
+// workgroups wait for nothing.  No result rests on that: every wait is
+// bounded (spin_ticks), and a down workgroup whose wait gives up computes
+// its split's s values itself, bitwise as the gate/up workgroups do (the
+// same code on the same data), before going on; the slice tail covers a
+// tail workgroup that gave up (down_finish).  Each such wait adds one to
+// counters[kFallbackSlot].  The arrival word counts gate/up workgroups in
+// its low half and down workgroups (one 1 << 16 each, after their wait) in
+// its high half; whichever arrival is the last of them all resets it, so a
+// late arrival can never leave it nonzero for the next launch.
 // ------------------------------------------------------------------------
 constexpr int kS2Waves = 4;
 constexpr int kS2Rows = 16;                           // down rows per wave, all in flight
 constexpr int kS2Ranks = kS2Waves * kS2Rows;          // ranks per split
 constexpr int kS2GuPerSplit = kS2Ranks / 4;           // gate/up workgroups (4 ranks each) per split
 
-// thread 0 only: waits until *ctr >= target; false on timeout
-
 template <typename T, typename TW>
 __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
     const T *__restrict__ x, int d, int F, const TW *__restrict__ w_gu, const float *__restrict__ gsc,
     const TW *__restrict__ wdt, const float *__restrict__ dsc, const int32_t *__restrict__ sel, int k, int n_gu,
     int n_slices, int S, float *__restrict__ s_sp, float *__restrict__ part, const T *residual, T *out,
-    uint32_t *__restrict__ counters, int32_t *__restrict__ iota_out, int act)
+    uint32_t *__restrict__ counters, int32_t *__restrict__ iota_out, int act, uint64_t spin_ticks)
 {
     constexpr int V = WRows<TW>::DV;
     constexpr int COLS = 64 * V;
     extern __shared__ float dyn[];  // gate/up: x [d]; down: red [kS2Waves][1][COLS]
-    __shared__ int s_flag;
+    __shared__ int s_flags[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
 
     if ((int)blockIdx.x < n_gu) {
         gateup_block<T, TW, 1, true>(x, 1, d, F, w_gu, gsc, sel, k, s_sp, iota_out, dyn, blockIdx.x, act);
         __builtin_amdgcn_s_waitcnt(0);  // this thread's s stores have completed
         __syncthreads();
-        if (tid == 0)
-            __hip_atomic_fetch_add(&counters[s2_sync_line(blockIdx.x / kS2GuPerSplit)], 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            const int sp = blockIdx.x / kS2GuPerSplit;
+            const uint32_t total = (uint32_t)min(kS2GuPerSplit, n_gu - sp * kS2GuPerSplit) + ((uint32_t)n_slices << 16);
+            uint32_t *line = &counters[s2_sync_line(sp)];
+            if (atomic_add_agent(line, 1u) + 1u == total)
+                __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         return;
     }
 
     // ---- down: (slice sl, split s) over ranks [64 s, 64 s + 64)
     const int dw = (int)blockIdx.x - n_gu;
     const int sl = dw % n_slices, s = dw / n_slices;
+    const int gu0 = s * kS2GuPerSplit, gu1 = min(n_gu, gu0 + kS2GuPerSplit);  // the split's gate/up workgroups
     if (tid == 0) {
-        uint32_t *ready = &counters[s2_sync_line(s)], *consumed = ready + 16;
-        const int r_end = min(k, (s + 1) * kS2Ranks);
-        const uint32_t target = (uint32_t)((r_end + 3) / 4 - s * kS2GuPerSplit);
-        if (!spin_wait_geq(ready, target))
-            __hip_atomic_store(&counters[kS2TimeoutSlot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__hip_atomic_fetch_add(consumed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)n_slices - 1) {  // every down workgroup of the split has passed the wait
-            __hip_atomic_store(ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(consumed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        uint32_t *line = &counters[s2_sync_line(s)];
+        const uint32_t total = (uint32_t)(gu1 - gu0) + ((uint32_t)n_slices << 16);
+        const bool ok = spin_wait_geq(line, (uint32_t)(gu1 - gu0), spin_ticks, 0xFFFFu);
+        if (!ok) atomic_add_agent(&counters[kFallbackSlot], 1u);
+        s_flags[0] = ok ? 0 : 1;
+        if (atomic_add_agent(line, 1u << 16) + (1u << 16) == total)
+            __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    if (uniform(s_flags[0])) {  // the wait gave up: the split's s values computed here
+        for (int b = gu0; b < gu1; ++b) {
+            __syncthreads();  // x in LDS no longer read by the previous block
+            gateup_block<T, TW, 1, true>(x, 1, d, F, w_gu, gsc, sel, k, s_sp, iota_out, dyn, b, act);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
     const int c = sl * COLS + lane * V;
     const int cc = c < d ? c : 0;
     const int rw0 = (s * kS2Waves + wv) * kS2Rows;  // this wave's first rank
@@ -530,9 +583,11 @@ __global__ __launch_bounds__(64 * kS2Waves) void stage2_fused_kernel(
             }
         }
     }
-    down_finish<T, V, 1, kS2Waves, 2>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), &s_flag, sl, s, 1, d,
+    __syncthreads();  // dyn (x of a fallback) free before it holds the wave sums
+    down_finish<T, V, 1, kS2Waves, 2>(acc, *reinterpret_cast<float(*)[kS2Waves][1][COLS]>(dyn), s_flags, sl, s, 1, d,
                                       S, part, dsc, residual, out, &counters[kDownSliceBase + sl],
-                                      &counters[kDownPassBase + sl], &counters[kS2TimeoutSlot]);
+                                      &counters[kDownPassBase + sl], &counters[kDownClaimBase + sl],
+                                      &counters[kFallbackSlot], spin_ticks);
 }
 
 // out = residual (or 0): the k == 0 case
@@ -682,35 +737,33 @@ hipError_t launch_down(int dtype, const S2Weights &w, const DownPlan &pl, const 
 template <typename T, typename TW>
 static hipError_t stage2_fused_t(const void *x, int d, int F, const S2Weights &w, const int32_t *sel, int k,
                                  float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
-                                 int32_t *iota_out, hipStream_t st)
+                                 int32_t *iota_out, hipStream_t st, uint64_t spin_ticks)
 {
     constexpr int V = WRows<TW>::DV;
     const int n_gu = (k + 3) / 4;
     const int n_slices = (d + 64 * V - 1) / (64 * V);
     const int S = (k + kS2Ranks - 1) / kS2Ranks;
-    if (S > kS2MaxSplits || n_slices > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
+    // slice words within [kDownSliceBase, kDownSliceEnd) and 32 claim bits;
+    // at most 1 << 15 down workgroups per split line
+    if (S > kS2MaxSplits || n_slices > kDownSliceEnd - kDownSliceBase) return hipErrorInvalidValue;
     const dim3 grid(n_gu + n_slices * S);
     const size_t lds = sizeof(float) * (size_t)max(xpad_row<gu_xpad<TW, 1>()>(d), kS2Waves * 64 * V);
     stage2_fused_kernel<T, TW><<<grid, 64 * kS2Waves, lds, st>>>(
         (const T *)x, d, F, (const TW *)w.w_gu, w.gu_scales, (const TW *)w.w_down_t, w.down_scales, sel, k, n_gu,
-        n_slices, S, s_sp, part, (const T *)residual, (T *)out, counters, iota_out, w.act);
+        n_slices, S, s_sp, part, (const T *)residual, (T *)out, counters, iota_out, w.act,
+        spin_ticks ? spin_ticks : kDefaultSpinTicks);
     return hipGetLastError();
 }
 
 hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int d, int F, const int32_t *sel, int k,
                                float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
-                               int32_t *iota_out, hipStream_t st)
+                               int32_t *iota_out, hipStream_t st, uint64_t spin_ticks)
 {
     if (k <= 0) return hipErrorInvalidValue;
-    if (w.fmt == 1)
-        return dtype == 0 ? stage2_fused_t<float, uint8_t>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
-                                                           iota_out, st)
-                          : stage2_fused_t<uint16_t, uint8_t>(x, d, F, w, sel, k, s_sp, part, residual, out,
-                                                              counters, iota_out, st);
-    return dtype == 0 ? stage2_fused_t<float, float>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
-                                                     iota_out, st)
-                      : stage2_fused_t<uint16_t, uint16_t>(x, d, F, w, sel, k, s_sp, part, residual, out, counters,
-                                                           iota_out, st);
+#define S2F(T, TW) stage2_fused_t<T, TW>(x, d, F, w, sel, k, s_sp, part, residual, out, counters, iota_out, st, spin_ticks)
+    if (w.fmt == 1) return dtype == 0 ? S2F(float, uint8_t) : S2F(uint16_t, uint8_t);
+    return dtype == 0 ? S2F(float, float) : S2F(uint16_t, uint16_t);
+#undef S2F
 }
 
 // ------------------------------------------------------------------------

@@ -1,6 +1,7 @@
-// Stage 2 of Prox ("Sparse Execution": exact gate/up, SiLU-multiply and the
-// down projection on the selected channels) for batches of 2..16 tokens with
-// bf16 activations, on the matrix cores.
+// Stage 2 of Prox (technical summary, "Stage 2: Exact Sparse Computation":
+// exact gate/up, SiLU-multiply and the down projection on the selected
+// channels) for batches of 2..16 tokens with bf16 activations, on the matrix
+// cores.
 //
 // At B tokens each weight byte feeds B multiply-adds; at B = 16 that is above
 // what the vector ALUs sustain at HBM speed, so both projections run on
@@ -400,8 +401,8 @@ __global__ __launch_bounds__(512) void dn_batch_kernel(const uint16_t *__restric
                                                        int F, const TW *__restrict__ wdt,
                                                        const float *__restrict__ dsc, const int32_t *__restrict__ sel,
                                                        int kps, int S, float *__restrict__ part,
-                                                       const uint16_t *__restrict__ residual,
-                                                       uint16_t *__restrict__ out, uint32_t *__restrict__ counters)
+                                                       const uint16_t *residual,  // may alias out
+                                                       uint16_t *out, uint32_t *__restrict__ counters)
 {
     constexpr int NC = DnRows<TW>::NC;
     constexpr int COLS = 16 * NC;
@@ -602,7 +603,7 @@ hipError_t launch_stage2_batch(const S2Weights &w, const void *x, int B, int d, 
                                int32_t *iota_out, hipStream_t st)
 {
     if (k <= 0 || B < 2 || B > kBT) return hipErrorInvalidValue;
-    if (pl.kps > kDnMaxKps || pl.n_ct > kS2TimeoutSlot - kDownSliceBase) return hipErrorInvalidValue;
+    if (pl.kps > kDnMaxKps || pl.n_ct > kDownSliceEnd - kDownSliceBase) return hipErrorInvalidValue;
     const dim3 ggrid(pl.n_full + (pl.n_tiles - pl.n_full) * pl.SK), dgrid(pl.S, pl.n_ct);
     const uint16_t *xp = (const uint16_t *)x;
     // x through the LDS tile above 8 tokens (see gu_batch_kernel)

@@ -30,6 +30,7 @@ SYMBOLS = (
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
     "prox_ffn_forward_ex", "prox_stage2_exact_ex", "prox_effective_sparsity", "prox_allocate_sparsity",
+    "prox_workspace_check",
 )
 
 
@@ -47,7 +48,7 @@ class _CWeights(ctypes.Structure):
 
 
 class _COptions(ctypes.Structure):
-    _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int)]
+    _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int), ("wait_limit_ticks", ctypes.c_int64)]
 
 
 class _CCostModel(ctypes.Structure):
@@ -92,6 +93,7 @@ def load_library(path: str = LIB_PATH):
         "prox_quantize_proxy": ([PW, I32, P, P, P], I32),
         "prox_workspace_size": ([I64, I64, I64, I32, PS], I32),
         "prox_workspace_init": ([P, ctypes.c_size_t, P], I32),
+        "prox_workspace_check": ([P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), P], I32),
         "prox_ffn_forward": ([P, I64, PW, PP, F, F, P, P, P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward_residual": ([P, I64, PW, PP, F, F, P, P, P, P, ctypes.c_size_t, P], I32),
         "prox_ffn_forward_timed": ([P, I64, PW, PP, F, F, P, P, P, ctypes.c_size_t, P, P], I32),
@@ -280,6 +282,16 @@ def workspace_init(ws: torch.Tensor) -> torch.Tensor:
     return ws
 
 
+def workspace_check(ws: torch.Tensor) -> int:
+    """Synchronize ws's stream and read its counters: raises ProxError if a
+    ticket or arrival counter is left nonzero; returns the number of bounded
+    waits that gave up (their results are still exact)."""
+    lib = load_library()
+    n = ctypes.c_uint32()
+    _check(lib.prox_workspace_check(_ptr(ws), ws.numel(), ctypes.byref(n), _stream(ws.device)), "prox_workspace_check")
+    return n.value
+
+
 def alloc_workspace(d: int, F: int, batch: int, mode: str = "int8_row", device="cuda", extra: int = 0):
     ws = torch.empty(workspace_size(d, F, batch, mode) + extra, dtype=torch.uint8, device=device)
     return workspace_init(ws)
@@ -291,12 +303,14 @@ def _mode_name(p: Proxy) -> str:
 
 def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sparsity: float,
                 out: torch.Tensor = None, sel_out: torch.Tensor = None, workspace: torch.Tensor = None,
-                residual: torch.Tensor = None, activation: str = "silu", signal: str = "s") -> torch.Tensor:
+                residual: torch.Tensor = None, activation: str = "silu", signal: str = "s",
+                wait_limit_ticks: int = 0) -> torch.Tensor:
     """The Prox FFN forward on x[B][d]; returns out[B][d] (out = residual + y if residual is given).
 
     activation: "silu" (SwiGLU) or "gelu_tanh" (GeGLU); signal: the channel
     selection signal, "s" (Prox), "h" / "u" (one proxy branch) or "exact_s"
-    (the exact state, no proxy; p may then be None)."""
+    (the exact state, no proxy; p may then be None).  wait_limit_ticks: the
+    bound of Stage 2's cross-workgroup waits in 10 ns ticks (0: default)."""
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
@@ -305,8 +319,8 @@ def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sp
     if workspace is None:
         workspace = alloc_workspace(w.d_model, w.d_ff, B, _mode_name(p) if p is not None else "int8_row", x.device)
     cw = w.c()
-    if activation != "silu" or signal != "s":
-        opt = _COptions(ACTIVATIONS[activation], SIGNALS[signal])
+    if activation != "silu" or signal != "s" or wait_limit_ticks:
+        opt = _COptions(ACTIVATIONS[activation], SIGNALS[signal], wait_limit_ticks)
         st = lib.prox_ffn_forward_ex(_ptr(x), B, ctypes.byref(cw), ctypes.byref(p.c()) if p is not None else None,
                                      input_keep, ffn_sparsity, ctypes.byref(opt), _ptr(residual), _ptr(out),
                                      _ptr(sel_out), _ptr(workspace), workspace.numel(), _stream(x.device))
@@ -376,7 +390,8 @@ def topk(scores: torch.Tensor, k: int) -> torch.Tensor:
 
 
 def stage2_exact(x: torch.Tensor, w: Weights, sel: torch.Tensor, out: torch.Tensor = None,
-                 workspace: torch.Tensor = None, activation: str = "silu") -> torch.Tensor:
+                 workspace: torch.Tensor = None, activation: str = "silu",
+                 wait_limit_ticks: int = 0) -> torch.Tensor:
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
@@ -386,8 +401,8 @@ def stage2_exact(x: torch.Tensor, w: Weights, sel: torch.Tensor, out: torch.Tens
         workspace = alloc_workspace(w.d_model, w.d_ff, B, "int8_row", x.device)
     cw = w.c()
     sel = sel.to(torch.int32).contiguous() if sel.numel() else sel
-    if activation != "silu":
-        opt = _COptions(ACTIVATIONS[activation], 0)
+    if activation != "silu" or wait_limit_ticks:
+        opt = _COptions(ACTIVATIONS[activation], 0, wait_limit_ticks)
         _check(lib.prox_stage2_exact_ex(_ptr(x), B, ctypes.byref(cw), _ptr(sel) if sel.numel() else None,
                                         sel.numel(), ctypes.byref(opt), _ptr(out), _ptr(workspace),
                                         workspace.numel(), _stream(x.device)), "prox_stage2_exact_ex")

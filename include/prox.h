@@ -25,12 +25,16 @@
  *  - Shapes: d_model % 8 == 0 (int4-g128 proxy: % 128), d_ff % 16 == 0,
  *    8 <= d_model <= 16384, 16 <= d_ff <= 65520, 1 <= batch <= 16
  *    (int4-g128 proxy: batch <= 4); other sizes return PROX_ERR_UNSUPPORTED.
+ *    The method targets single-token decoding and names large batches as
+ *    beyond its scope (technical summary, "Significance and Claims"): one
+ *    token is the tuned case, small batches share one mask.
  *  - One workspace must not be used by two calls that may run concurrently.
  *    Its first 278528 bytes hold counters that must be zero before the
  *    workspace's first use (prox_workspace_init, or any zero fill); every
- *    call leaves them zero again.  After a call that returned PROX_ERR_HIP
- *    its kernels may have stopped part-way: zero them again before the next
- *    use.  The rest means nothing between calls.
+ *    call leaves them zero again, except one word counting bounded waits
+ *    that gave up (prox_workspace_check).  After a call that returned
+ *    PROX_ERR_HIP its kernels may have stopped part-way: zero them again
+ *    before the next use.  The rest means nothing between calls.
  *
  * Notation: d = d_model, F = d_ff, B = batch, bf16 = bfloat16 bit patterns.
  */
@@ -210,6 +214,17 @@ prox_status prox_workspace_size(int64_t d_model, int64_t d_ff, int64_t batch, pr
  * workgroup with ticket counters that each call returns to zero. */
 prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Health of a workspace after the calls enqueued before this one on the
+ * stream (host-only; synchronizes the stream).  Reads the counter block:
+ * *fallbacks receives the number of bounded waits that gave up since the
+ * workspace was last zeroed (each was completed without the awaited data, so
+ * no result was wrong).  Returns PROX_ERR_WORKSPACE if any ticket or arrival
+ * counter is nonzero, i.e. a call stopped part-way (after PROX_ERR_HIP) and
+ * the workspace needs prox_workspace_init before its next use; PROX_ERR_HIP if
+ * the copy or the synchronization fails. */
+prox_status prox_workspace_check(const void *workspace, size_t workspace_bytes, uint32_t *fallbacks,
+                                 hipStream_t stream);
+
 /* The Prox FFN forward (both stages).
  *   x   [B][d] device, w->dtype: the FFN input (already normalized).
  *   out [B][d] device, w->dtype: y = sum over selected j of W_down[:, j] *
@@ -252,9 +267,16 @@ typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
  * Each is summed over the batch before the top-k. */
 typedef enum { PROX_SIGNAL_S = 0, PROX_SIGNAL_H = 1, PROX_SIGNAL_U = 2, PROX_SIGNAL_EXACT_S = 3 } prox_signal;
 
+/* wait_limit_ticks: the single-token Stage 2 hands work between its
+ * workgroups through bounded waits.  A wait gives up after this many ticks
+ * of the device's 100 MHz real-time counter (0: half a second); the
+ * workgroup then computes what it waited for itself, so the result is the
+ * same, bitwise, only later.  Each wait that gives up adds one to the count
+ * prox_workspace_check reports.  Negative: PROX_ERR_INVALID_ARG. */
 typedef struct {
     prox_activation activation;
     prox_signal signal;
+    int64_t wait_limit_ticks;
 } prox_options;
 
 /* prox_ffn_forward with options (opt NULL = SILU and S, i.e. prox_ffn_forward)
@@ -282,7 +304,10 @@ prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weig
                                    int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream, hipEvent_t *events);
 
-/* Stage 1 alone: the mask, and optionally the fp32 channel scores.
+/* Stage 1 alone (technical summary, "Stage 1: Lightweight Proxy
+ * Construction": sparsify x by magnitude, proxy gate/up projections with the
+ * quantized weights, salience |silu(g~) u~|, top-k channels): the mask, and
+ * optionally the fp32 channel scores.
  *   sel_idx_out: device int32 [k] ascending (k from prox_counts);
  *   scores_out:  nullable device fp32 [F] (score_j as above).
  * Requires k < F (k == F needs no Stage 1). */
@@ -299,7 +324,10 @@ prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights 
 prox_status prox_topk(const float *scores, int64_t n, int64_t k, int32_t *sel_idx_out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Stage 2 alone: exact masked SwiGLU on a given mask.
+/* Stage 2 alone (technical summary, "Stage 2: Exact Sparse Computation": the
+ * gate and up projections with the original weights and the dense x on the
+ * selected channels, the SiLU-multiply, then the down projection over the
+ * same channels): exact masked SwiGLU on a given mask.
  *   sel_idx [k] device int32, distinct channels in [0, F) in ascending order
  *   (entries outside [0, F) are clamped into it: wrong values, no stray
  *   access); out [B][d] device.  0 <= k <= F. */
@@ -307,14 +335,17 @@ prox_status prox_stage2_exact(const void *x, int64_t batch, const prox_weights *
                               const int32_t *sel_idx, int64_t k, void *out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
-/* prox_stage2_exact with options (only the activation applies; opt NULL =
- * SILU). */
+/* prox_stage2_exact with options (the activation and the wait limit apply;
+ * opt NULL = SILU and the default limit). */
 prox_status prox_stage2_exact_ex(const void *x, int64_t batch, const prox_weights *w,
                                  const int32_t *sel_idx, int64_t k, const prox_options *opt, void *out,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* RMSNorm with unit gain: out = h / sqrt(mean(h^2) + eps), fp32 math, rounded
- * to the dtype.  h, out [B][d] device (may alias). */
+ * to the dtype.  h, out [B][d] device (may alias).  1 <= B <= 4096; d % 8 ==
+ * 0 and 8 <= d <= 16384, else PROX_ERR_UNSUPPORTED; eps >= 0 and not NaN.
+ * (The pages do not describe the layers around the FFN; this is the glue of
+ * the layer stack below.) */
 prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d_model, prox_dtype dtype, float eps,
                          void *out, hipStream_t stream);
 

@@ -53,7 +53,8 @@ def unpack_proxy(p: P.Proxy):
 
 
 class Layer:
-    """One seeded SwiGLU FFN layer on host (synth arrays) and device (packed)."""
+    """One seeded SwiGLU FFN layer on host (synth arrays) and device (packed).
+    drop_host() frees the host arrays once the oracle no longer needs them."""
 
     def __init__(self, d, F, std, dtype, seed=0, layer=0, pattern=None):
         self.d, self.F, self.dtype = d, F, dtype
@@ -72,6 +73,10 @@ class Layer:
         if mode not in self._proxy:
             self._proxy[mode] = P.quantize_proxy(self.w, mode)
         return self._proxy[mode]
+
+    def drop_host(self):
+        self.wg = self.wu = self.wd = None
+        self._oproxy = {}
 
     def oracle_proxy(self, mode):
         if mode not in self._oproxy:
@@ -99,7 +104,10 @@ def run_and_check(layer: Layer, x_host: np.ndarray, mode: str, keep: float, sp: 
     k_in, k = P.counts(layer.d, layer.F, keep, sp)
     sel_t = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
     res_t = to_dev(residual) if residual is not None else None
-    out = P.ffn_forward(x, layer.w, layer.proxy(mode), keep, sp, sel_out=sel_t, residual=res_t)
+    ws = P.alloc_workspace(layer.d, layer.F, B, mode)
+    out = P.ffn_forward(x, layer.w, layer.proxy(mode), keep, sp, sel_out=sel_t, residual=res_t, workspace=ws)
+    # counters back at zero, and no bounded wait gave up
+    assert P.workspace_check(ws) == 0, "%s: a bounded wait gave up" % label
     torch.cuda.synchronize()
     y_gpu = from_dev(out)
     sel_gpu = sel_t[:k].cpu().numpy().astype(np.int64)
@@ -118,4 +126,4 @@ def run_and_check(layer: Layer, x_host: np.ndarray, mode: str, keep: float, sp: 
     err_own = out_error(y_gpu, y_own) if k > 0 else err
     log("%s k_in=%d k=%d mask %s err=%.3g err_vs_oracle_mask=%.3g" % (label, k_in, k, msg, err, err_own))
     assert err <= TOL[layer.dtype], "%s output error %.3g > %.3g" % (label, err, TOL[layer.dtype])
-    return dict(err=err, err_own=err_own, sel=sel_gpu, y=y_gpu, ref=ref)
+    return dict(err=err, err_own=err_own, sel=sel_gpu, y=y_gpu, ref=ref, out=out)

@@ -160,6 +160,9 @@ def test_other_entry_points_reject(lib):
                                   v(FAKE + 256), 1 << 40, None) == B.ERR_INVALID_ARG  # k == F: no Stage 1
     assert lib.prox_rmsnorm(v(FAKE), 1, 4096, 9, 1e-5, v(FAKE), None) == B.ERR_UNSUPPORTED
     assert lib.prox_rmsnorm(v(FAKE), 1, 4096, B.BF16, float("nan"), v(FAKE), None) == B.ERR_INVALID_ARG
+    for d in (16392, 1001, 4100, 4, 65536):  # beyond the row the kernel holds, or not whole 16-byte vectors
+        assert lib.prox_rmsnorm(v(FAKE), 1, d, B.BF16, 1e-5, v(FAKE), None) == B.ERR_UNSUPPORTED
+        assert lib.prox_rmsnorm(v(FAKE), 2, d, B.F32, 1e-5, v(FAKE), None) == B.ERR_UNSUPPORTED
     assert lib.prox_pack_weights(v(FAKE), v(FAKE), v(0), 4096, 14336, B.BF16, v(FAKE), v(FAKE),
                                  None) == B.ERR_INVALID_ARG
     assert lib.prox_quantize_proxy(ctypes.byref(w), 3, v(FAKE), v(FAKE), None) == B.ERR_UNSUPPORTED
@@ -169,6 +172,15 @@ def test_other_entry_points_reject(lib):
                                        v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
         assert lib.prox_stage2_exact_ex(v(FAKE), 1, ctypes.byref(w), v(FAKE + 64), 5, ctypes.byref(opt),
                                         v(FAKE + 128), v(FAKE + 256), 1 << 40, None) == B.ERR_UNSUPPORTED
+    opt = B._COptions(0, 0, -1)  # a negative wait limit
+    assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
+                                   v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_INVALID_ARG
+    assert lib.prox_stage2_exact_ex(v(FAKE), 1, ctypes.byref(w), v(FAKE + 64), 5, ctypes.byref(opt),
+                                    v(FAKE + 128), v(FAKE + 256), 1 << 40, None) == B.ERR_INVALID_ARG
+    n = ctypes.c_uint32()
+    assert lib.prox_workspace_check(None, 1 << 20, ctypes.byref(n), None) == B.ERR_INVALID_ARG
+    assert lib.prox_workspace_check(v(FAKE), 1 << 20, None, None) == B.ERR_INVALID_ARG
+    assert lib.prox_workspace_check(v(FAKE), 4096, ctypes.byref(n), None) == B.ERR_WORKSPACE
     opt = B._COptions(0, 1)  # a proxy signal needs the proxy
     assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), None, 0.5, 0.7, ctypes.byref(opt), None,
                                    v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_INVALID_ARG
