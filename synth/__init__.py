@@ -22,6 +22,7 @@ bf16 tensors are returned as ``uint16`` bit patterns; float32 tensors as
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -61,11 +62,16 @@ def _normal_matrix(rows: int, cols: int, std: float, dtype: str, rng: np.random.
 
 
 def make_weights(d: int, F: int, std: float, dtype: str, seed: int = 0, layer: int = 0):
-    """(w_gate[F][d], w_up[F][d], w_down[d][F]) in nn.Linear orientation."""
+    """(w_gate[F][d], w_up[F][d], w_down[d][F]) in nn.Linear orientation.
+
+    The three matrices come from independent streams, so they are drawn in
+    three threads (NumPy fills and converts large arrays without the GIL);
+    the values do not depend on it."""
     assert dtype in ("f32", "bf16")
-    wg = _normal_matrix(F, d, std, dtype, _rng(seed, layer, ROLE_GATE))
-    wu = _normal_matrix(F, d, std, dtype, _rng(seed, layer, ROLE_UP))
-    wd = _normal_matrix(d, F, std, dtype, _rng(seed, layer, ROLE_DOWN))
+    jobs = ((F, d, ROLE_GATE), (F, d, ROLE_UP), (d, F, ROLE_DOWN))
+    with ThreadPoolExecutor(max_workers=3) as ex:
+        futs = [ex.submit(_normal_matrix, r, c, std, dtype, _rng(seed, layer, role)) for r, c, role in jobs]
+        wg, wu, wd = [f.result() for f in futs]
     return wg, wu, wd
 
 

@@ -1,0 +1,136 @@
+"""The 32-layer stack of 8B-like FFN layers, h <- h + FFN_l(RMSNorm(h)),
+at B = 1 and B = 8, and the layer glue on small shapes.
+
+Full depth, teacher-forced: every layer's GPU input (the GPU's h, and its
+RMSNorm from prox_rmsnorm) is handed to the oracle for that layer, and the
+two acceptance rules (mask within the near-tie window, output within the
+bf16 tolerance against the oracle's Stage 2 on the GPU's mask) are checked
+at each of the 32 layers.  The layers run in blocks of four, one test each,
+so that progress shows while the host draws 15 GB of weights.  Then the
+single chain call over all 32 layers must equal that layer-by-layer
+composition bitwise, and the end-to-end drift against an oracle-only chain
+from the same h0 is reported (not gated: a near-tie mask flip in one layer
+legitimately changes every later layer).
+
+Small shapes cover the other branches of the chain: fp32 layers, the int4
+proxy inside the single-token Stage 1 with the norm, d_ff above the fused
+Stage 1's limit (the stand-alone input selection with the norm), and
+sparsity 0 (dense layers with an RMSNorm launch)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import free_sparse_swiglu_stage1_amd as P
+from tests.gpu_util import Layer, from_dev, log, run_and_check, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS["llama8b_chain32"]
+EPS = 1e-5
+N_LAYERS = 32
+BLOCK = 4
+_state = {}
+
+
+def _host(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _init_state():
+    if not _state:
+        _state["layers"] = []  # device weights and proxies of every layer
+        _state["h0"] = {B: synth.make_x(B, W.d, W.dtype, seed=0, layer=99) for B in W.batches}
+        _state["h"] = {B: to_dev(_state["h0"][B]) for B in W.batches}          # GPU chain, layer by layer
+        _state["h_ref"] = {B: oracle.as_f64(_state["h0"][B]) for B in W.batches}  # oracle-only chain
+        _state["done"] = 0
+    return _state
+
+
+@pytest.mark.parametrize("block", range(N_LAYERS // BLOCK))
+def test_chain32_teacher_forced(block):
+    st = _init_state()
+    assert st["done"] == block * BLOCK, "blocks run in order"
+    for l in range(block * BLOCK, (block + 1) * BLOCK):
+        L = Layer(W.d, W.F, W.std, W.dtype, seed=0, layer=l)
+        for B in W.batches:
+            h = st["h"][B]
+            xn = P.rmsnorm(h, EPS)
+            torch.cuda.synchronize()
+            h_host, xn_host = _host(h), _host(xn)
+            # RMSNorm in fp32 rounded to bf16: within one bf16 rounding of the oracle's
+            rr = oracle.rmsnorm(h_host, EPS)
+            assert np.abs(oracle.as_f64(xn_host) - rr).max() <= 2.0 ** -8 * np.abs(rr).max()
+            r = run_and_check(L, xn_host, W.mode, W.input_keep, W.sparsities[0], residual=h_host,
+                              label="chain32 B=%d layer %d" % (B, l))
+            st["h"][B] = r["out"]
+            # the oracle-only chain: its own norm, mask and output on its own h
+            hr = st["h_ref"][B]
+            ref = oracle.prox_forward(oracle.rmsnorm(hr, EPS), L.wg, L.wu, L.wd, L.oracle_proxy(W.mode),
+                                      W.input_keep, W.sparsities[0], W.mode)
+            st["h_ref"][B] = hr + ref["y"]
+        L.drop_host()
+        st["layers"].append((L.w, L.proxy(W.mode)))
+        st["done"] = l + 1
+    torch.cuda.synchronize()
+
+
+def test_chain32_single_call_bitwise_and_drift():
+    st = _init_state()
+    if st["done"] != N_LAYERS:
+        pytest.skip("the teacher-forced blocks did not all run")
+    ws_list, ps_list = [w for w, _ in st["layers"]], [p for _, p in st["layers"]]
+    drift = {}
+    for B in W.batches:
+        h_chain = to_dev(st["h0"][B])
+        ws = P.workspace_init(torch.empty(P.chain_workspace_size(W.d, W.F, B, W.mode), dtype=torch.uint8,
+                                          device="cuda"))
+        P.chain_forward(h_chain, ws_list, ps_list, W.input_keep, W.sparsities[0], eps=EPS, workspace=ws)
+        assert P.workspace_check(ws) == 0
+        assert torch.equal(h_chain.view(torch.int16), st["h"][B].view(torch.int16)), "B=%d" % B
+        y_gpu, y_ref = from_dev(h_chain), st["h_ref"][B]
+        per_tok = [float(np.abs(y_gpu[b] - y_ref[b]).max() / np.abs(y_ref[b]).max()) for b in range(B)]
+        drift[str(B)] = {"max_rel_err_per_token": max(per_tok), "mean_rel_err_per_token": float(np.mean(per_tok)),
+                         "h_maxabs": float(np.abs(y_ref).max())}
+        log("chain32 B=%d end-to-end drift vs the oracle-only chain: max %.3g, mean %.3g"
+            % (B, max(per_tok), float(np.mean(per_tok))))
+    if os.path.isdir("gpurun_out"):
+        with open(os.path.join("gpurun_out", "chain32_drift.json"), "w") as f:
+            json.dump(drift, f, indent=1)
+    _state.clear()
+
+
+# ----------------------------------------------------------- small shapes
+
+@pytest.mark.parametrize("d,F,dt,mode,sp,B", [
+    (512, 1376, "f32", "int8_row", 0.5, 1),      # fp32 norm inside the single-token Stage 1
+    (512, 1376, "f32", "int8_row", 0.5, 3),      # fp32 norm inside the batch input selection
+    (1024, 2048, "bf16", "int4_g128", 0.7, 1),   # int4 proxy, single-token Stage 1 with the norm
+    (1024, 2048, "bf16", "int4_g128", 0.7, 2),
+    (1024, 16400, "bf16", "int8_row", 0.7, 1),   # d_ff beyond the fused Stage 1: input selection with the norm
+    (1024, 2048, "bf16", "int8_row", 0.0, 1),    # dense layers: an RMSNorm launch per layer
+    (1024, 2048, "bf16", "int8_row", 0.0, 4),
+])
+def test_chain_small_equals_composition(d, F, dt, mode, sp, B):
+    n = 3
+    Ls = [Layer(d, F, 0.05, dt, seed=7, layer=l) for l in range(n)]
+    h0 = synth.make_x(B, d, dt, seed=8)
+    # layer-by-layer composition, layer 0 checked against the oracle
+    h = to_dev(h0)
+    for l, L in enumerate(Ls):
+        xn = P.rmsnorm(h, EPS)
+        if l == 0:
+            torch.cuda.synchronize()
+            h_host = h.cpu().numpy() if dt == "f32" else _host(h)
+            xn_host = xn.cpu().numpy() if dt == "f32" else _host(xn)
+            run_and_check(L, xn_host, mode, 0.5, sp, residual=h_host, label="chain small l0")
+        h = P.ffn_forward(xn, L.w, L.proxy(mode), 0.5, sp, residual=h)
+    hc = to_dev(h0)
+    ws = P.workspace_init(torch.empty(P.chain_workspace_size(d, F, B, mode), dtype=torch.uint8, device="cuda"))
+    P.chain_forward(hc, [L.w for L in Ls], [L.proxy(mode) for L in Ls], 0.5, sp, eps=EPS, workspace=ws)
+    assert P.workspace_check(ws) == 0
+    assert torch.equal(hc.view(torch.uint8), h.view(torch.uint8))

@@ -2,9 +2,8 @@
 launch configuration the benchmark times: the 512x1376 fp32 toy layer, the
 7B-like 4096x11008 layer (0/50/70/90% sparsity), the 8B-like 4096x14336
 layer (B = 1, 4, 16), the 70B-like 8192x28672 layer (int4-g128 and int8
-proxies, 50/70/90%), and a stack of 8B-like layers with RMSNorm and residual
-adds (teacher-forced per layer, B = 1 and 8).  The oracle computes every
-output element at these sizes."""
+proxies, 50/70/90%).  The oracle computes every output element at these
+sizes.  The 32-layer stack of 8B-like layers is in test_gpu_chain.py."""
 import numpy as np
 import pytest
 import torch
@@ -57,30 +56,3 @@ def test_llama70b(mode, sp):
     w = W["llama70b"]
     run_and_check(layer("llama70b"), synth.make_x(1, w.d, w.dtype, seed=0), mode, w.input_keep, sp,
                   label="llama70b %s sp=%g" % (mode, sp))
-
-
-@pytest.mark.parametrize("B", W["llama8b_chain32"].batches)
-def test_chain_teacher_forced(B):
-    """Layers of the 8B-like stack, h <- h + FFN(RMSNorm(h)).  Each layer is
-    checked against the oracle on the GPU's own input to that layer; the
-    chain entry point must equal the layer-by-layer composition bitwise."""
-    w = W["llama8b_chain32"]
-    n_layers = 3
-    Ls = [layer("llama8b", 0)] + [layer("llama8b_chain32", l) for l in range(1, n_layers)]
-    h0 = synth.make_x(B, w.d, w.dtype, seed=0, layer=99)
-    h = to_dev(h0)
-    for l, L in enumerate(Ls):
-        xn = P.rmsnorm(h, 1e-5)
-        torch.cuda.synchronize()
-        h_host = h.view(torch.int16).cpu().numpy().view(np.uint16)
-        xn_host = xn.view(torch.int16).cpu().numpy().view(np.uint16)
-        # RMSNorm in fp32 rounded to bf16: within one bf16 rounding of the oracle's
-        rr = oracle.rmsnorm(h_host, 1e-5)
-        assert np.abs(oracle.as_f64(xn_host) - rr).max() <= 2.0 ** -8 * np.abs(rr).max()
-        run_and_check(L, xn_host, w.mode, w.input_keep, w.sparsities[0], residual=h_host,
-                      label="chain B=%d layer %d" % (B, l))
-        h = P.ffn_forward(xn, L.w, L.proxy(w.mode), w.input_keep, w.sparsities[0], residual=h)
-    h_chain = to_dev(h0)
-    P.chain_forward(h_chain, [L.w for L in Ls], [L.proxy(w.mode) for L in Ls], w.input_keep, w.sparsities[0])
-    torch.cuda.synchronize()
-    assert torch.equal(h_chain.view(torch.int16), h.view(torch.int16))
