@@ -47,10 +47,22 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                                               "-o", tmp] + sources()
+LIB_SAN = os.path.join(HERE, "libprox_san.so")
+
+# The host code (argument checks, workspace layout, launch sequence) under
+# AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as
+# usual.  Each sanitizer flag applies to the host pass only.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, extra_flags=None, sanitize: bool = False) -> str:
+    out = LIB_SAN if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    flags = HIPCC_FLAGS + (SANITIZE_FLAGS if sanitize else [])
+    cmd = [hipcc()] + flags + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                                                         "-o", tmp] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -60,8 +72,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + r.stdout)
     if verbose and r.stdout.strip():
         print(r.stdout)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

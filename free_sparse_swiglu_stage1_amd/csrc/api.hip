@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "../../include/prox.h"
 #include "kernels.h"
@@ -31,12 +32,24 @@ constexpr int kTargetProxyBlocks = 1024;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// An enum the caller passed (a field or a parameter) read as the int it is
+// in the C interface: a caller may hand over any int, and loading a C++
+// enum object holding a value outside the enumeration is undefined.
+template <typename E>
+int enum_int(const E &e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are ints");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 prox_status hip_status(hipError_t e) { return e == hipSuccess ? PROX_OK : PROX_ERR_HIP; }
 
 bool bad_ptr(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) != 0; }
 bool bad_ptr_opt(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
 
-int elem_bytes(prox_dtype t) { return t == PROX_F32 ? 4 : 2; }
+int elem_bytes(int t) { return t == PROX_F32 ? 4 : 2; }
 
 prox_status check_shape(int64_t d, int64_t F)
 {
@@ -57,14 +70,14 @@ prox_status check_mode_shape(int64_t d, int64_t F, int mode)
 prox_status check_weights(const prox_weights *w)
 {
     if (!w) return PROX_ERR_INVALID_ARG;
-    if (w->dtype != PROX_F32 && w->dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    if (enum_int(w->dtype) != PROX_F32 && enum_int(w->dtype) != PROX_BF16) return PROX_ERR_UNSUPPORTED;
     prox_status s = check_shape(w->d_model, w->d_ff);
     if (s != PROX_OK) return s;
     if (bad_ptr(w->w_gu) || bad_ptr(w->w_down_t)) return PROX_ERR_INVALID_ARG;
-    if (w->wformat == PROX_W_FP8_E4M3) {
+    if (enum_int(w->wformat) == PROX_W_FP8_E4M3) {
         if (w->d_model % 16 != 0) return PROX_ERR_UNSUPPORTED;
         if (bad_ptr(w->gu_scales) || bad_ptr(w->down_scales)) return PROX_ERR_INVALID_ARG;
-    } else if (w->wformat != PROX_W_NATIVE) {
+    } else if (enum_int(w->wformat) != PROX_W_NATIVE) {
         return PROX_ERR_UNSUPPORTED;
     }
     return PROX_OK;
@@ -75,23 +88,26 @@ struct Opts {
     int act = PROX_ACT_SILU;
     int signal = PROX_SIGNAL_S;
     uint64_t spin_ticks = 0;  // 0: the kernels' default bound
+    int flags = 0;
 };
 
 prox_status check_options(const prox_options *o, Opts *out)
 {
     if (!o) return PROX_OK;
-    if (o->activation != PROX_ACT_SILU && o->activation != PROX_ACT_GELU_TANH) return PROX_ERR_UNSUPPORTED;
-    if (o->signal < PROX_SIGNAL_S || o->signal > PROX_SIGNAL_EXACT_S) return PROX_ERR_UNSUPPORTED;
+    if (enum_int(o->activation) != PROX_ACT_SILU && enum_int(o->activation) != PROX_ACT_GELU_TANH) return PROX_ERR_UNSUPPORTED;
+    if (enum_int(o->signal) < PROX_SIGNAL_S || enum_int(o->signal) > PROX_SIGNAL_EXACT_S) return PROX_ERR_UNSUPPORTED;
     if (o->wait_limit_ticks < 0) return PROX_ERR_INVALID_ARG;
-    out->act = o->activation;
-    out->signal = o->signal;
+    if (o->flags & ~PROX_FLAG_SINGLE_LAUNCH) return PROX_ERR_UNSUPPORTED;
+    out->act = enum_int(o->activation);
+    out->signal = enum_int(o->signal);
     out->spin_ticks = (uint64_t)o->wait_limit_ticks;
+    out->flags = o->flags;
     return PROX_OK;
 }
 
 S2Weights s2_weights(const prox_weights *w, int act)
 {
-    const bool fp8 = w->wformat == PROX_W_FP8_E4M3;
+    const bool fp8 = enum_int(w->wformat) == PROX_W_FP8_E4M3;
     return S2Weights{fp8 ? 1 : 0, w->w_gu, fp8 ? w->gu_scales : nullptr, w->w_down_t,
                      fp8 ? w->down_scales : nullptr, act};
 }
@@ -100,7 +116,7 @@ prox_status check_proxy(const prox_proxy *p, const prox_weights *w)
 {
     if (!p) return PROX_ERR_INVALID_ARG;
     if (p->d_model != w->d_model || p->d_ff != w->d_ff) return PROX_ERR_INVALID_ARG;
-    prox_status s = check_mode_shape(p->d_model, p->d_ff, p->mode);
+    prox_status s = check_mode_shape(p->d_model, p->d_ff, enum_int(p->mode));
     if (s != PROX_OK) return s;
     if (bad_ptr(p->codes) || bad_ptr(p->scales)) return PROX_ERR_INVALID_ARG;
     return PROX_OK;
@@ -157,7 +173,7 @@ ProxyPlan proxy_plan(int64_t d, int64_t F, int64_t B, int mode)
 DownPlan down_plan(int64_t d, int64_t k, int64_t B, const prox_weights *w)
 {
     DownPlan p;
-    p.vec = w->wformat == PROX_W_FP8_E4M3 ? 8 : 16 / elem_bytes(w->dtype);  // FP8: 8-byte loads
+    p.vec = enum_int(w->wformat) == PROX_W_FP8_E4M3 ? 8 : 16 / elem_bytes(enum_int(w->dtype));  // FP8: 8-byte loads
     p.cols = 64 * p.vec;
     p.n_slices = ceil_div(d, p.cols);
     p.S = ceil_div(k > 0 ? k : 1, kDownRowsPerWave * kDownWaves);
@@ -167,6 +183,9 @@ DownPlan down_plan(int64_t d, int64_t k, int64_t B, const prox_weights *w)
 
 struct Workspace {
     uint32_t *counters;
+    float *lk_part;   // single-launch layer: proxy block partials
+    uint32_t *lk_selw; // single-launch layer: the published selection
+    float *lk_ypart;  // single-launch layer: per-workgroup partial outputs
     float *xh;
     float *proxy_part;
     float *score;
@@ -211,9 +230,39 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
         w.s_pieces = nullptr;
         w.bdn_part = nullptr;
     }
+    if (B == 1 && (d == 4096 || d == 8192) && F <= kFusedMaxF) {  // the single-launch layer
+        w.lk_part = (float *)take(sizeof(float) * (size_t)kLayerMaxGroups * 2048);
+        w.lk_selw = (uint32_t *)take(sizeof(uint32_t) * 1024);  // the published selection
+        w.lk_ypart = (float *)take(sizeof(float) * (size_t)kLayerMaxGroups * d);
+    } else {
+        w.lk_part = w.lk_ypart = nullptr;
+        w.lk_selw = nullptr;
+    }
     w.bytes = off;
     return w;
 }
+
+// The single-launch layer serves bf16 tokens with bf16 weights and an int8
+// proxy where the device runs it (layer_groups) and the shape fits.
+int layer_path(int64_t B, const prox_weights *w, const prox_proxy *p, int64_t k_in, int64_t k, const Opts &o)
+{
+    if (!(o.flags & PROX_FLAG_SINGLE_LAUNCH)) return 0;
+    if (B != 1 || enum_int(w->dtype) != PROX_BF16 || enum_int(w->wformat) != PROX_W_NATIVE || !p || enum_int(p->mode) != PROX_Q_INT8_ROW) return 0;
+    if (o.signal == PROX_SIGNAL_EXACT_S) return 0;
+    const int G = layer_groups();
+    return layer_supported(B, w->d_model, w->d_ff, k_in, k, G) ? G : 0;
+}
+
+prox_status run_layer(const void *x, const prox_weights *w, const prox_proxy *p, int64_t k_in, int64_t k,
+                      const void *residual, void *out, int32_t *sel_out, const Workspace &ws, hipStream_t st,
+                      const Opts &o, int G)
+{
+    return hip_status(launch_layer(x, (int)w->d_model, (int)w->d_ff, (int)k_in, (int)k, (const uint8_t *)p->codes,
+                                   (const float *)p->scales, w->w_gu, w->w_down_t, residual, out, sel_out, ws.lk_part,
+                                   ws.score, ws.lk_selw, ws.lk_ypart, ws.counters, o.act, o.signal, o.spin_ticks,
+                                   G, st));
+}
+
 
 #define TRY_HIP(expr)                                           \
     do {                                                        \
@@ -233,23 +282,23 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
                        void *xn = nullptr)
 {
     const int64_t d = w->d_model, F = w->d_ff;
-    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    const int dt = enum_int(w->dtype) == PROX_F32 ? 0 : 1;
     if (fused_supported(B, d, F)) {  // one kernel; its counters are zero on entry
         TRY_HIP(mark(ev, 0, st));
-        TRY_HIP(launch_stage1_fused(dt, p->mode == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
+        TRY_HIP(launch_stage1_fused(dt, enum_int(p->mode) == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
                                     (const uint8_t *)p->codes, (const float *)p->scales, ws.proxy_part, score, sel,
                                     ws.counters, o.act, o.signal, st, norm_eps, xn));
         TRY_HIP(mark(ev, 1, st));
         return hip_status(mark(ev, 2, st));
     }
-    const ProxyPlan pp = proxy_plan(d, F, B, p->mode);
+    const ProxyPlan pp = proxy_plan(d, F, B, enum_int(p->mode));
     TRY_HIP(mark(ev, 0, st));
     TRY_HIP(launch_xselect(dt, x, (int)B, (int)d, (int)k_in, ws.xh, ws.counters,
                            kTicketWords, st, norm_eps, xn));
     TRY_HIP(mark(ev, 1, st));
     // bf16 batches above 4 tokens, int8 codes: the matrix cores (at 4 tokens
     // the vector-ALU kernel is faster, 32.6 against 35.3 us at 4096 x 14336)
-    if (dt == 1 && p->mode == PROX_Q_INT8_ROW && B > 4)
+    if (dt == 1 && enum_int(p->mode) == PROX_Q_INT8_ROW && B > 4)
         TRY_HIP(launch_proxy_batch(ws.xh, (int)B, (int)d, (int)F, (const uint8_t *)p->codes,
                                    (const float *)p->scales, ws.proxy_part, score, ws.counters, o.act, o.signal, st));
     else
@@ -265,7 +314,7 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
                        const void *residual, void *out, int32_t *iota_out, const Workspace &ws, hipStream_t st,
                        hipEvent_t *ev = nullptr, const Opts &o = Opts())
 {
-    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    const int dt = enum_int(w->dtype) == PROX_F32 ? 0 : 1;
     const int64_t d = w->d_model;
     const S2Weights sw = s2_weights(w, o.act);
     TRY_HIP(mark(ev, 3, st));
@@ -303,7 +352,7 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
 prox_status run_exact_signal(const void *x, int64_t B, const prox_weights *w, int64_t k, int32_t *sel,
                              const void *residual, void *out, const Workspace &ws, hipStream_t st, const Opts &o)
 {
-    const int dt = w->dtype == PROX_F32 ? 0 : 1;
+    const int dt = enum_int(w->dtype) == PROX_F32 ? 0 : 1;
     const int64_t d = w->d_model, F = w->d_ff;
     const S2Weights sw = s2_weights(w, o.act);
     TRY_HIP(launch_gateup(dt, sw, x, (int)B, (int)d, (int)F, nullptr, (int)F, ws.s_sp, nullptr, st));
@@ -327,12 +376,12 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     s = check_weights(w);
     if (s != PROX_OK) return s;
     const bool exact = o.signal == PROX_SIGNAL_EXACT_S;  // no proxy is read
-    const int mode = exact ? (p ? (int)p->mode : (int)PROX_Q_INT8_ROW) : -1;
+    const int mode = exact ? (p ? (int)enum_int(p->mode) : (int)PROX_Q_INT8_ROW) : -1;
     if (!exact || p) {
         s = check_proxy(p, w);
         if (s != PROX_OK) return s;
     }
-    s = check_batch(B, exact ? mode : p->mode);
+    s = check_batch(B, exact ? mode : enum_int(p->mode));
     if (s != PROX_OK) return s;
     if (bad_ptr(x) || bad_ptr(out) || bad_ptr_opt(sel_out) || bad_ptr_opt(residual) || bad_ptr(workspace))
         return PROX_ERR_INVALID_ARG;
@@ -340,7 +389,7 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     int64_t k_in, k;
     s = counts(w->d_model, w->d_ff, keep, sp, &k_in, &k);
     if (s != PROX_OK) return s;
-    const Workspace ws = layout(w->d_model, w->d_ff, B, exact ? mode : p->mode, workspace);
+    const Workspace ws = layout(w->d_model, w->d_ff, B, exact ? mode : enum_int(p->mode), workspace);
     if (ws_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
     const int64_t F = w->d_ff;
     if (k == 0 || k == F) {  // no Stage 1
@@ -351,6 +400,13 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     }
     int32_t *sel = sel_out ? sel_out : ws.sel;
     if (exact) return run_exact_signal(x, B, w, k, sel, residual, out, ws, st, o);
+    if (const int G = layer_path(B, w, p, k_in, k, o)) {  // both stages in one launch
+        TRY_HIP(mark(ev, 0, st));
+        s = run_layer(x, w, p, k_in, k, residual, out, sel_out, ws, st, o, G);
+        if (s != PROX_OK) return s;
+        for (int i = 1; i < 6; ++i) TRY_HIP(mark(ev, i, st));
+        return PROX_OK;
+    }
     s = run_stage1(x, B, w, p, k_in, k, sel, ws.score, ws, st, ev, o);
     if (s != PROX_OK) return s;
     return run_stage2(x, B, w, sel, k, residual, out, nullptr, ws, st, ev, o);
@@ -424,12 +480,13 @@ prox_status prox_allocate_sparsity(const prox_cost_model *m, double target, doub
 prox_status prox_pack_weights(const void *w_gate, const void *w_up, const void *w_down, int64_t d, int64_t F,
                               prox_dtype dtype, void *w_gu_out, void *w_down_t_out, hipStream_t stream)
 {
-    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    const int dtype_i = enum_int(dtype);
+    if (dtype_i != PROX_F32 && dtype_i != PROX_BF16) return PROX_ERR_UNSUPPORTED;
     prox_status s = check_shape(d, F);
     if (s != PROX_OK) return s;
     if (bad_ptr(w_gate) || bad_ptr(w_up) || bad_ptr(w_down) || bad_ptr(w_gu_out) || bad_ptr(w_down_t_out))
         return PROX_ERR_INVALID_ARG;
-    return hip_status(launch_pack(dtype == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F, w_gu_out,
+    return hip_status(launch_pack(dtype_i == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F, w_gu_out,
                                   w_down_t_out, stream));
 }
 
@@ -437,24 +494,26 @@ prox_status prox_pack_weights_fp8(const void *w_gate, const void *w_up, const vo
                                   prox_dtype dtype, void *w_gu_out, float *gu_scales_out, void *w_down_t_out,
                                   float *down_scales_out, hipStream_t stream)
 {
-    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    const int dtype_i = enum_int(dtype);
+    if (dtype_i != PROX_F32 && dtype_i != PROX_BF16) return PROX_ERR_UNSUPPORTED;
     prox_status s = check_shape(d, F);
     if (s != PROX_OK) return s;
     if (d % 16 != 0) return PROX_ERR_UNSUPPORTED;
     if (bad_ptr(w_gate) || bad_ptr(w_up) || bad_ptr(w_down) || bad_ptr(w_gu_out) || bad_ptr(gu_scales_out) ||
         bad_ptr(w_down_t_out) || bad_ptr(down_scales_out))
         return PROX_ERR_INVALID_ARG;
-    return hip_status(launch_pack_fp8(dtype == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F,
+    return hip_status(launch_pack_fp8(dtype_i == PROX_F32 ? 0 : 1, w_gate, w_up, w_down, (int)d, (int)F,
                                       (uint8_t *)w_gu_out, gu_scales_out, (uint8_t *)w_down_t_out, down_scales_out,
                                       stream));
 }
 
 prox_status prox_proxy_sizes(int64_t d, int64_t F, prox_qmode mode, size_t *codes_bytes, size_t *scales_bytes)
 {
+    const int mode_i = enum_int(mode);
     if (!codes_bytes || !scales_bytes) return PROX_ERR_INVALID_ARG;
-    prox_status s = check_mode_shape(d, F, mode);
+    prox_status s = check_mode_shape(d, F, mode_i);
     if (s != PROX_OK) return s;
-    if (mode == PROX_Q_INT8_ROW) {
+    if (mode_i == PROX_Q_INT8_ROW) {
         *codes_bytes = (size_t)d * 2 * F;
         *scales_bytes = sizeof(float) * 2 * F;
     } else {
@@ -467,24 +526,26 @@ prox_status prox_proxy_sizes(int64_t d, int64_t F, prox_qmode mode, size_t *code
 prox_status prox_quantize_proxy(const prox_weights *w, prox_qmode mode, void *codes, void *scales,
                                 hipStream_t stream)
 {
+    const int mode_i = enum_int(mode);
     prox_status s = check_weights(w);
     if (s != PROX_OK) return s;
-    s = check_mode_shape(w->d_model, w->d_ff, mode);
+    s = check_mode_shape(w->d_model, w->d_ff, mode_i);
     if (s != PROX_OK) return s;
     if (bad_ptr(codes) || bad_ptr(scales)) return PROX_ERR_INVALID_ARG;
-    return hip_status(launch_quantize(w->dtype == PROX_F32 ? 0 : 1, w->wformat == PROX_W_FP8_E4M3 ? 1 : 0, w->w_gu,
-                                      w->gu_scales, mode == PROX_Q_INT4_G128 ? 4 : 8, (int)w->d_model, (int)w->d_ff,
+    return hip_status(launch_quantize(enum_int(w->dtype) == PROX_F32 ? 0 : 1, enum_int(w->wformat) == PROX_W_FP8_E4M3 ? 1 : 0, w->w_gu,
+                                      w->gu_scales, mode_i == PROX_Q_INT4_G128 ? 4 : 8, (int)w->d_model, (int)w->d_ff,
                                       (uint8_t *)codes, (float *)scales, stream));
 }
 
 prox_status prox_workspace_size(int64_t d, int64_t F, int64_t B, prox_qmode mode, size_t *bytes)
 {
+    const int mode_i = enum_int(mode);
     if (!bytes) return PROX_ERR_INVALID_ARG;
-    prox_status s = check_mode_shape(d, F, mode);
+    prox_status s = check_mode_shape(d, F, mode_i);
     if (s != PROX_OK) return s;
-    s = check_batch(B, mode);
+    s = check_batch(B, mode_i);
     if (s != PROX_OK) return s;
-    *bytes = layout(d, F, B, mode, nullptr).bytes;
+    *bytes = layout(d, F, B, mode_i, nullptr).bytes;
     return PROX_OK;
 }
 
@@ -510,9 +571,11 @@ prox_status prox_workspace_check(const void *workspace, size_t workspace_bytes, 
     }
     bool clean = true;
     for (int i = 0; i < kZeroWords; ++i)
-        if (i != kFallbackSlot && h[i] != 0u) clean = false;
+        if (i != kFallbackSlot && i != kLayerErrorSlot && h[i] != 0u) clean = false;
     *fallbacks = h[kFallbackSlot];
+    const bool failed = h[kLayerErrorSlot] != 0u;
     free(h);
+    if (failed) return PROX_ERR_HIP;
     return clean ? PROX_OK : PROX_ERR_WORKSPACE;
 }
 
@@ -562,7 +625,7 @@ prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights 
     if (s != PROX_OK) return s;
     s = check_proxy(p, w);
     if (s != PROX_OK) return s;
-    s = check_batch(batch, p->mode);
+    s = check_batch(batch, enum_int(p->mode));
     if (s != PROX_OK) return s;
     if (bad_ptr(x) || bad_ptr(sel_idx_out) || bad_ptr_opt(scores_out) || bad_ptr(workspace))
         return PROX_ERR_INVALID_ARG;
@@ -570,7 +633,7 @@ prox_status prox_stage1_select(const void *x, int64_t batch, const prox_weights 
     s = counts(w->d_model, w->d_ff, input_keep, ffn_sparsity, &k_in, &k);
     if (s != PROX_OK) return s;
     if (k == w->d_ff) return PROX_ERR_INVALID_ARG;
-    const Workspace ws = layout(w->d_model, w->d_ff, batch, p->mode, workspace);
+    const Workspace ws = layout(w->d_model, w->d_ff, batch, enum_int(p->mode), workspace);
     if (workspace_bytes < ws.bytes) return PROX_ERR_WORKSPACE;
     return run_stage1(x, batch, w, p, k_in, k, sel_idx_out, scores_out ? scores_out : ws.score, ws, stream);
 }
@@ -614,12 +677,13 @@ prox_status prox_stage2_exact_ex(const void *x, int64_t batch, const prox_weight
 prox_status prox_rmsnorm(const void *h, int64_t batch, int64_t d, prox_dtype dtype, float eps, void *out,
                          hipStream_t stream)
 {
-    if (dtype != PROX_F32 && dtype != PROX_BF16) return PROX_ERR_UNSUPPORTED;
+    const int dtype_i = enum_int(dtype);
+    if (dtype_i != PROX_F32 && dtype_i != PROX_BF16) return PROX_ERR_UNSUPPORTED;
     if (batch < 1 || batch > 4096 || isnan(eps) || eps < 0.0f) return PROX_ERR_INVALID_ARG;
     // the kernel holds a row in 16-byte vectors, at most 16384 elements
     if (d < 8 || d > 16384 || d % 8 != 0) return PROX_ERR_UNSUPPORTED;
     if (bad_ptr(h) || bad_ptr(out)) return PROX_ERR_INVALID_ARG;
-    return hip_status(launch_rmsnorm(dtype == PROX_F32 ? 0 : 1, h, (int)batch, (int)d, eps, out, stream));
+    return hip_status(launch_rmsnorm(dtype_i == PROX_F32 ? 0 : 1, h, (int)batch, (int)d, eps, out, stream));
 }
 
 prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layers, const prox_proxy *proxies,
@@ -635,32 +699,32 @@ prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layer
         if (s != PROX_OK) return s;
         s = check_proxy(&proxies[l], &layers[l]);
         if (s != PROX_OK) return s;
-        if (layers[l].d_model != w0.d_model || layers[l].d_ff != w0.d_ff || layers[l].dtype != w0.dtype ||
-            proxies[l].mode != proxies[0].mode)
+        if (layers[l].d_model != w0.d_model || layers[l].d_ff != w0.d_ff || enum_int(layers[l].dtype) != enum_int(w0.dtype) ||
+            enum_int(proxies[l].mode) != enum_int(proxies[0].mode))
             return PROX_ERR_INVALID_ARG;
     }
-    prox_status s = check_batch(batch, proxies[0].mode);
+    prox_status s = check_batch(batch, enum_int(proxies[0].mode));
     if (s != PROX_OK) return s;
     int64_t k_in, k;
     s = counts(w0.d_model, w0.d_ff, input_keep, ffn_sparsity, &k_in, &k);
     if (s != PROX_OK) return s;
     size_t ffn_bytes = 0;
-    s = prox_workspace_size(w0.d_model, w0.d_ff, batch, proxies[0].mode, &ffn_bytes);
+    s = prox_workspace_size(w0.d_model, w0.d_ff, batch, proxies[0].mode, &ffn_bytes);  // checked valid above
     if (s != PROX_OK) return s;
     const size_t need = ffn_bytes + 256 + (size_t)batch * w0.d_model * 4;
     if (workspace_bytes < need) return PROX_ERR_WORKSPACE;
     void *xn = (char *)workspace + align256(ffn_bytes);
-    const int dt = w0.dtype == PROX_F32 ? 0 : 1;
+    const int dt = enum_int(w0.dtype) == PROX_F32 ? 0 : 1;
     if (k > 0 && k < w0.d_ff) {
         // Stage 1's first kernel (the single-token kernel, or the input
         // selection of a batch) normalizes h itself, bitwise as the RMSNorm
         // kernel, and hands RMSNorm(h) to Stage 2 in xn: no RMSNorm launch
-        const Workspace ws = layout(w0.d_model, w0.d_ff, batch, proxies[0].mode, workspace);
+        const Workspace ws = layout(w0.d_model, w0.d_ff, batch, enum_int(proxies[0].mode), workspace);
         const bool fused = batch == 1 && fused_supported(1, w0.d_model, w0.d_ff);
         for (int64_t l = 0; l < n_layers; ++l) {
             const prox_proxy &p = proxies[l];
             if (fused) {
-                TRY_HIP(launch_stage1_fused(dt, p.mode == PROX_Q_INT4_G128 ? 4 : 8, h, (int)w0.d_model,
+                TRY_HIP(launch_stage1_fused(dt, enum_int(p.mode) == PROX_Q_INT4_G128 ? 4 : 8, h, (int)w0.d_model,
                                             (int)w0.d_ff, (int)k_in, (int)k, (const uint8_t *)p.codes,
                                             (const float *)p.scales, ws.proxy_part, ws.score, ws.sel, ws.counters,
                                             PROX_ACT_SILU, PROX_SIGNAL_S, stream, eps, xn));

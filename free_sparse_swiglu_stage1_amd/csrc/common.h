@@ -273,8 +273,26 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// The NW per-wave words at `p` (LDS, 16-byte aligned, NW a multiple of 4)
+// read with 16-byte reads, all issued before any is used: a loop of single
+// reads would wait for each in turn.
+template <int NW>
+__device__ __forceinline__ void lds_words(const uint32_t *p, uint32_t (&v)[NW])
+{
+    static_assert(NW % 4 == 0, "whole 16-byte reads");
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+        const u32x4 q = reinterpret_cast<const u32x4 *>(p)[i];
+        v[4 * i] = q.x;
+        v[4 * i + 1] = q.y;
+        v[4 * i + 2] = q.z;
+        v[4 * i + 3] = q.w;
+    }
+}
+
 // Exclusive prefix sum over the block in thread order; returns the block
-// total through *total.  scratch: >= NW uint32 in LDS.  All threads call.
+// total through *total.  scratch: >= NW uint32 in LDS, 16-byte aligned.  All
+// threads call.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratch, uint32_t *total)
 {
@@ -284,12 +302,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
     const uint32_t incl = wave_incl_scan(v);
     if (lane == kWave - 1) scratch[wid] = incl;
     __syncthreads();
+    uint32_t sw[NW];
+    lds_words<NW>(scratch, sw);
     uint32_t base = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const uint32_t s = scratch[w];
-        base += (w < wid) ? s : 0u;
-        tot += s;
+        base += (w < wid) ? sw[w] : 0u;
+        tot += sw[w];
     }
     __syncthreads();
     *total = tot;
@@ -308,11 +327,14 @@ __device__ __forceinline__ uint32_t block_and_or(uint32_t a, uint32_t o, uint32_
         scratch[NW + wid] = o;
     }
     __syncthreads();
+    uint32_t wa[NW], wo[NW];
+    lds_words<NW>(scratch, wa);
+    lds_words<NW>(scratch + NW, wo);
     uint32_t ra = 0xFFFFFFFFu, ro = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        ra &= scratch[w];
-        ro |= scratch[NW + w];
+        ra &= wa[w];
+        ro |= wo[w];
     }
     __syncthreads();
     *or_out = ro;

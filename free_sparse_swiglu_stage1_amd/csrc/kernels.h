@@ -138,6 +138,10 @@ constexpr int kDownSliceBase = 512;
 constexpr int kDownSliceEnd = 1023;
 constexpr int kDownPassBase = 1024;
 constexpr int kDownClaimBase = 1536;
+constexpr int kLayerBarrierSlot = 2045;  // the single-launch layer's grid-barrier arrivals
+constexpr int kLayerErrorSlot = 2046;    // its grid-barrier waits that gave up (not reset by kernels)
+constexpr int kLayerBlockSyncBase = 2048;  // its per-block barriers: arrivals, passes; one pair per 64 words
+constexpr int kLayerBlockSyncStride = 64;
 constexpr int kFallbackSlot = 2047;
 constexpr int kS2SyncBase = 4096;
 constexpr int kS2SyncPages = 64;
@@ -157,6 +161,23 @@ hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int
                                int32_t *iota_out, hipStream_t st, uint64_t spin_ticks = 0);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
 
+// The whole forward for one bf16 token (bf16 weights, int8 proxy) in one
+// launch of G workgroups, one per CU, all resident at once (layer.hip).  G
+// <= kLayerMaxGroups sizes the workspace areas: part G*2048 floats, selw
+// 1024 words, ypart G*d floats.  Counter slots: the per-block barrier words
+// at kLayerBlockSyncBase + kLayerBlockSyncStride * c (c < 16),
+// kFusedScoreSlot, kLayerBarrierSlot, kLayerErrorSlot and the release words
+// at s2_sync_line(w), w < G.  residual may alias out.
+constexpr int kLayerMaxGroups = 256;
+bool layer_supported(int64_t B, int64_t d, int64_t F, int64_t k_in, int64_t k, int G);
+hipError_t launch_layer(const void *x, int d, int F, int k_in, int k, const uint8_t *codes, const float *qscales,
+                        const void *w_gu, const void *w_dt, const void *residual, void *out, int32_t *sel_out,
+                        float *part, float *score, uint32_t *selw, float *ypart, uint32_t *counters, int act,
+                        int signal, uint64_t spin_ticks, int G, hipStream_t st);
+// Workgroups the single-launch layer uses on the current device (one per
+// CU, at most kLayerMaxGroups), or 0 if it cannot run there (a CU does not
+// hold one of its 1024-thread workgroups).
+int layer_groups();
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
 
 hipError_t launch_pack(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,

@@ -50,7 +50,7 @@ struct alignas(16) SelectSmem {
     static_assert(MAXN % 64 == 0 && W <= kPassBins, "bitmap sizes");
     uint32_t hist[kPassBins * kHistCopiesMax];  // radix counters; afterwards the bitmap of keys equal to T
     uint32_t bits[W];          // selection bitmap: bit i of word i/32 = index i selected
-    uint32_t scratch[64];
+    alignas(16) uint32_t scratch[64];
     uint32_t found[4];
 };
 
@@ -77,12 +77,13 @@ __device__ __forceinline__ uint32_t waves_excl_scan(uint32_t wave_val, uint32_t 
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) scratch[wid] = wave_val;
     __syncthreads();
+    uint32_t sw[NW];
+    lds_words<NW>(scratch, sw);
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const uint32_t s = scratch[w];
-        before += (w < wid) ? s : 0u;
-        tot += s;
+        before += (w < wid) ? sw[w] : 0u;
+        tot += sw[w];
     }
     __syncthreads();
     *total = tot;
@@ -107,8 +108,10 @@ __device__ __forceinline__ void find_crossing(const uint32_t (&h)[BPT], uint32_t
     if (lane == 0) scratch[wv] = wtot;
     __syncthreads();
     uint32_t a = wtot - incl;  // keys in this wave's higher threads
+    uint32_t sw[NW];
+    lds_words<NW>(scratch, sw);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) a += (w > wv) ? scratch[w] : 0u;
+    for (int w = 0; w < NW; ++w) a += (w > wv) ? sw[w] : 0u;
     if (a < remaining && remaining <= a + local) {
         bool done = false;
 #pragma unroll

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void proxy_kernel(const float *__restrict__ xh
     __shared__ int li[kMaxSplitRange];
     __shared__ float lx[kMaxSplitRange * NB];
     __shared__ float gsc[QBITS == 4 ? NG : 1][2][QBITS == 4 ? CB : 1];
-    __shared__ uint32_t scr[64];
+    __shared__ __align__(16) uint32_t scr[64];
     __shared__ float red[4][2][CB];
     __shared__ int s_last;
 

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void proxy_batch_kernel(const float *__restric
 {
     __shared__ __align__(16) uint16_t xt[kPxMaxR / 32][4][16][8];  // [K-step][g][token][8 inputs], 32 KB
     __shared__ int lst[kPxMaxR];                                    // the listed inputs
-    __shared__ uint32_t scr[64];
+    __shared__ __align__(16) uint32_t scr[64];
     __shared__ int s_last;
     float *red = reinterpret_cast<float *>(&xt[0][0][0][0]);  // after the MFMAs: [2][16 tokens][2][128]
 

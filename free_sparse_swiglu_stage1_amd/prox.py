@@ -14,12 +14,14 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libprox.so")
+# PROX_LIB names another build of the library (the host-sanitized one)
+LIB_PATH = os.environ.get("PROX_LIB") or os.path.join(_HERE, "libprox.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 Q_INT8_ROW, Q_INT4_G128 = 0, 1
 W_NATIVE, W_FP8_E4M3 = 0, 1
+FLAG_SINGLE_LAUNCH = 1
 ACTIVATIONS = {"silu": 0, "gelu_tanh": 1}
 SIGNALS = {"s": 0, "h": 1, "u": 2, "exact_s": 3}
 MODES = {"int8_row": Q_INT8_ROW, "int4_g128": Q_INT4_G128}
@@ -48,7 +50,8 @@ class _CWeights(ctypes.Structure):
 
 
 class _COptions(ctypes.Structure):
-    _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int), ("wait_limit_ticks", ctypes.c_int64)]
+    _fields_ = [("activation", ctypes.c_int), ("signal", ctypes.c_int), ("wait_limit_ticks", ctypes.c_int64),
+                ("flags", ctypes.c_int32)]
 
 
 class _CCostModel(ctypes.Structure):
@@ -304,13 +307,15 @@ def _mode_name(p: Proxy) -> str:
 def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sparsity: float,
                 out: torch.Tensor = None, sel_out: torch.Tensor = None, workspace: torch.Tensor = None,
                 residual: torch.Tensor = None, activation: str = "silu", signal: str = "s",
-                wait_limit_ticks: int = 0) -> torch.Tensor:
+                wait_limit_ticks: int = 0, single_launch: bool = False) -> torch.Tensor:
     """The Prox FFN forward on x[B][d]; returns out[B][d] (out = residual + y if residual is given).
 
     activation: "silu" (SwiGLU) or "gelu_tanh" (GeGLU); signal: the channel
     selection signal, "s" (Prox), "h" / "u" (one proxy branch) or "exact_s"
     (the exact state, no proxy; p may then be None).  wait_limit_ticks: the
-    bound of Stage 2's cross-workgroup waits in 10 ns ticks (0: default)."""
+    bound of cross-workgroup waits in 10 ns ticks (0: default).  single_launch:
+    both stages in one launch where the shape allows it (slower on MI355X;
+    see PROX_FLAG_SINGLE_LAUNCH)."""
     lib = load_library()
     _dev(x, "x")
     B = x.shape[0]
@@ -319,8 +324,9 @@ def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sp
     if workspace is None:
         workspace = alloc_workspace(w.d_model, w.d_ff, B, _mode_name(p) if p is not None else "int8_row", x.device)
     cw = w.c()
-    if activation != "silu" or signal != "s" or wait_limit_ticks:
-        opt = _COptions(ACTIVATIONS[activation], SIGNALS[signal], wait_limit_ticks)
+    if activation != "silu" or signal != "s" or wait_limit_ticks or single_launch:
+        opt = _COptions(ACTIVATIONS[activation], SIGNALS[signal], wait_limit_ticks,
+                        FLAG_SINGLE_LAUNCH if single_launch else 0)
         st = lib.prox_ffn_forward_ex(_ptr(x), B, ctypes.byref(cw), ctypes.byref(p.c()) if p is not None else None,
                                      input_keep, ffn_sparsity, ctypes.byref(opt), _ptr(residual), _ptr(out),
                                      _ptr(sel_out), _ptr(workspace), workspace.numel(), _stream(x.device))

@@ -267,16 +267,29 @@ typedef enum { PROX_ACT_SILU = 0, PROX_ACT_GELU_TANH = 1 } prox_activation;
  * Each is summed over the batch before the top-k. */
 typedef enum { PROX_SIGNAL_S = 0, PROX_SIGNAL_H = 1, PROX_SIGNAL_U = 2, PROX_SIGNAL_EXACT_S = 3 } prox_signal;
 
-/* wait_limit_ticks: the single-token Stage 2 hands work between its
- * workgroups through bounded waits.  A wait gives up after this many ticks
- * of the device's 100 MHz real-time counter (0: half a second); the
- * workgroup then computes what it waited for itself, so the result is the
- * same, bitwise, only later.  Each wait that gives up adds one to the count
- * prox_workspace_check reports.  Negative: PROX_ERR_INVALID_ARG. */
+/* wait_limit_ticks: workgroups of one launch hand work to each other through
+ * bounded waits.  A wait gives up after this many ticks of the device's
+ * 100 MHz real-time counter (0: half a second).  In the single-token Stage 2
+ * the workgroup then computes what it waited for itself, so the result is
+ * the same, bitwise, only later; each such wait adds one to the count
+ * prox_workspace_check reports.  The single-launch layer (below) waits on
+ * grid barriers of workgroups that are all resident; a wait there that gives
+ * up is a failure: the output is NaN and prox_workspace_check returns
+ * PROX_ERR_HIP.  Negative: PROX_ERR_INVALID_ARG.
+ * flags: PROX_FLAG_SINGLE_LAUNCH runs both stages of the layer in one launch
+ * of one 1024-thread workgroup per CU, its phases joined by grid barriers,
+ * where the shape allows it (one bf16 token, bf16 weights, int8 proxy,
+ * d_model 4096 or 8192, d_ff <= 16384); elsewhere it is ignored.  Its
+ * results agree with the default two-launch path within rounding, not
+ * bitwise.  On MI355X it is slower than the default (61 against 53.5 us at
+ * 4096 x 14336, 70% sparsity): the barriers cost more than the launch gap.
+ * Unknown flags: PROX_ERR_UNSUPPORTED. */
+#define PROX_FLAG_SINGLE_LAUNCH 1
 typedef struct {
     prox_activation activation;
     prox_signal signal;
     int64_t wait_limit_ticks;
+    int32_t flags;
 } prox_options;
 
 /* prox_ffn_forward with options (opt NULL = SILU and S, i.e. prox_ffn_forward)

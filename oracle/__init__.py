@@ -48,6 +48,23 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+_LIB_SAN = os.path.join(_HERE, "libprox_oracle_san.so")
+_CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build_sanitized() -> str:
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang, whose sanitizer runtime also serves the HIP library's sanitized
+    host build), for the host-sanitizer test run.  Same arithmetic flags."""
+    tmp = _LIB_SAN + ".tmp%d" % os.getpid()
+    subprocess.check_call([_CLANG, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm", "-L/opt/rocm/llvm/lib",
+                           "-Wl,-rpath,/opt/rocm/llvm/lib"])
+    os.replace(tmp, _LIB_SAN)
+    return _LIB_SAN
+
+
 def use_library(path=None) -> None:
     """Point the shim at another build of ``prox_oracle.c`` (None = the default).
 
@@ -61,8 +78,12 @@ def use_library(path=None) -> None:
 
 def _load():
     if _lib is None:
-        build(force=False)
-        _bind(ctypes.CDLL(_LIB))
+        alt = os.environ.get("PROX_ORACLE_LIB")  # another build of prox_oracle.c (the sanitized one)
+        if alt:
+            _bind(ctypes.CDLL(alt))
+        else:
+            build(force=False)
+            _bind(ctypes.CDLL(_LIB))
     return _lib
 
 

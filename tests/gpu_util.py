@@ -97,15 +97,16 @@ def out_error(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
 
 
 def run_and_check(layer: Layer, x_host: np.ndarray, mode: str, keep: float, sp: float, residual=None,
-                  label=""):
-    """Run the GPU forward and apply both acceptance rules.  Returns a dict of diagnostics."""
+                  label="", **fwd):
+    """Run the GPU forward (keyword options `fwd` passed on to ffn_forward) and
+    apply both acceptance rules.  Returns a dict of diagnostics."""
     B = x_host.shape[0]
     x = to_dev(x_host)
     k_in, k = P.counts(layer.d, layer.F, keep, sp)
     sel_t = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
     res_t = to_dev(residual) if residual is not None else None
     ws = P.alloc_workspace(layer.d, layer.F, B, mode)
-    out = P.ffn_forward(x, layer.w, layer.proxy(mode), keep, sp, sel_out=sel_t, residual=res_t, workspace=ws)
+    out = P.ffn_forward(x, layer.w, layer.proxy(mode), keep, sp, sel_out=sel_t, residual=res_t, workspace=ws, **fwd)
     # counters back at zero, and no bounded wait gave up
     assert P.workspace_check(ws) == 0, "%s: a bounded wait gave up" % label
     torch.cuda.synchronize()

@@ -172,6 +172,9 @@ def test_other_entry_points_reject(lib):
                                        v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
         assert lib.prox_stage2_exact_ex(v(FAKE), 1, ctypes.byref(w), v(FAKE + 64), 5, ctypes.byref(opt),
                                         v(FAKE + 128), v(FAKE + 256), 1 << 40, None) == B.ERR_UNSUPPORTED
+    opt = B._COptions(0, 0, 0, 2)  # an unknown flag
+    assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
+                                   v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
     opt = B._COptions(0, 0, -1)  # a negative wait limit
     assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
                                    v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_INVALID_ARG

@@ -30,6 +30,7 @@ def test_forced_wait_give_up_is_exact(d, F, std, sp, dt):
     ws = P.alloc_workspace(d, F, 1, mode)
     _, k = P.counts(d, F, 0.5, sp)
     sel = torch.empty(k, dtype=torch.int32, device="cuda")
+    # the default two-launch path, whose Stage 2 hands work over through bounded waits
     ref = P.ffn_forward(x, L.w, L.proxy(mode), 0.5, sp, sel_out=sel, workspace=ws)
     assert P.workspace_check(ws) == 0
     for rep in range(2):  # twice: the first forced run must leave the workspace clean for the next
