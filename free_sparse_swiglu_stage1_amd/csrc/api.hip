@@ -7,10 +7,18 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/prox.h"
 #include "kernels.h"
 
 using namespace prox;
+
+// The workspace of prox_ffn_forward_noalloc: one copy per device, held until
+// the process ends.  Host code never uses this name as an address (on the
+// host it stands for the symbol, not for device memory): the device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[PROX_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -412,6 +420,28 @@ prox_status forward_impl(const void *x, int64_t B, const prox_weights *w, const 
     return run_stage2(x, B, w, sel, k, residual, out, nullptr, ws, st, ev, o);
 }
 
+// The device address of `scratch` on the current device, its counters
+// cleared on the stream the first time (after that every call leaves them
+// at zero).  Thread-safe; the table holds one address per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+prox_status static_scratch(hipStream_t st, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PROX_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PROX_ERR_HIP;
+        TRY_HIP(launch_zero_u32((uint32_t *)ptr, kZeroWords, st));  // a kernel: capturable
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PROX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,6 +454,8 @@ const char *prox_status_string(int status)
     case PROX_ERR_UNSUPPORTED: return "PROX_ERR_UNSUPPORTED: unsupported shape, dtype, mode or batch";
     case PROX_ERR_WORKSPACE: return "PROX_ERR_WORKSPACE: workspace too small";
     case PROX_ERR_HIP: return "PROX_ERR_HIP: HIP launch failed";
+    case PROX_ERR_SCRATCH_LIMIT:
+        return "PROX_ERR_SCRATCH_LIMIT: the layer's workspace exceeds PROX_STATIC_SCRATCH_BYTES (use a workspace)";
     default: return "unknown prox status";
     }
 }
@@ -604,6 +636,24 @@ prox_status prox_ffn_forward_ex(const void *x, int64_t batch, const prox_weights
 {
     return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, residual, out, sel_idx_out, workspace,
                         workspace_bytes, stream, nullptr, opt);
+}
+
+prox_status prox_ffn_forward_noalloc(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,
+                                     float input_keep, float ffn_sparsity, const void *residual, void *out,
+                                     int32_t *sel_idx_out, hipStream_t stream)
+{
+    // the size limit first, on the host: nothing touches the device for a
+    // layer whose workspace the static array cannot hold
+    if (!w || !p) return PROX_ERR_INVALID_ARG;
+    size_t need = 0;
+    prox_status s = prox_workspace_size(w->d_model, w->d_ff, batch, p->mode, &need);
+    if (s != PROX_OK) return s;
+    if (need > (size_t)PROX_STATIC_SCRATCH_BYTES) return PROX_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    s = static_scratch(stream, &ws);
+    if (s != PROX_OK) return s;
+    return forward_impl(x, batch, w, p, input_keep, ffn_sparsity, residual, out, sel_idx_out, ws,
+                        (size_t)PROX_STATIC_SCRATCH_BYTES, stream);
 }
 
 prox_status prox_ffn_forward_timed(const void *x, int64_t batch, const prox_weights *w, const prox_proxy *p,

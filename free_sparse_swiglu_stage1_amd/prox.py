@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # PROX_LIB names another build of the library (the host-sanitized one)
 LIB_PATH = os.environ.get("PROX_LIB") or os.path.join(_HERE, "libprox.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5
+STATIC_SCRATCH_BYTES = 64 << 20  # PROX_STATIC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 Q_INT8_ROW, Q_INT4_G128 = 0, 1
 W_NATIVE, W_FP8_E4M3 = 0, 1
@@ -32,7 +33,7 @@ SYMBOLS = (
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
     "prox_ffn_forward_ex", "prox_stage2_exact_ex", "prox_effective_sparsity", "prox_allocate_sparsity",
-    "prox_workspace_check",
+    "prox_workspace_check", "prox_ffn_forward_noalloc",
 )
 
 
@@ -109,6 +110,7 @@ def load_library(path: str = LIB_PATH):
         "prox_stage2_exact_ex": ([P, I64, PW, P, I64, PO, P, P, ctypes.c_size_t, P], I32),
         "prox_effective_sparsity": ([PM, D, D, PD], I32),
         "prox_allocate_sparsity": ([PM, D, D, D, PD, PD], I32),
+        "prox_ffn_forward_noalloc": ([P, I64, PW, PP, F, F, P, P, P, P], I32),
     }
     for name in SYMBOLS:
         fn = getattr(lib, name)
@@ -341,6 +343,19 @@ def ffn_forward(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sp
                                            ffn_sparsity, _ptr(residual), _ptr(out), _ptr(sel_out),
                                            _ptr(workspace), workspace.numel(), _stream(x.device))
     _check(st, "prox_ffn_forward")
+    return out
+
+
+def ffn_forward_noalloc(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float, ffn_sparsity: float,
+                        out: torch.Tensor, sel_out: torch.Tensor = None, residual: torch.Tensor = None) -> torch.Tensor:
+    """ffn_forward on the library's own per-device workspace array: no device
+    memory is allocated by the library (out and sel_out are the caller's).
+    Calls that may overlap in time on one device race."""
+    lib = load_library()
+    _dev(x, "x")
+    st = lib.prox_ffn_forward_noalloc(_ptr(x), x.shape[0], ctypes.byref(w.c()), ctypes.byref(p.c()), input_keep,
+                                      ffn_sparsity, _ptr(residual), _ptr(out), _ptr(sel_out), _stream(x.device))
+    _check(st, "prox_ffn_forward_noalloc")
     return out
 
 

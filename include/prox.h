@@ -55,7 +55,9 @@ typedef enum {
     PROX_ERR_INVALID_ARG = -1, /* null/misaligned pointer, NaN or out-of-range fraction, bad batch */
     PROX_ERR_UNSUPPORTED = -2, /* shape, dtype or mode outside the supported set above */
     PROX_ERR_WORKSPACE = -3,   /* workspace_bytes smaller than prox_workspace_size() */
-    PROX_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+    PROX_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError) */
+    PROX_ERR_SCRATCH_LIMIT = -5 /* prox_ffn_forward_noalloc: the layer's workspace exceeds
+                                   PROX_STATIC_SCRATCH_BYTES */
 } prox_status;
 
 /* Element type of x, out and the full-precision weights (one type per call).
@@ -301,6 +303,28 @@ prox_status prox_ffn_forward_ex(const void *x, int64_t batch, const prox_weights
                                 const prox_options *opt, const void *residual, void *out,
                                 int32_t *sel_idx_out, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of prox_ffn_forward_residual (residual nullable) without a workspace
+ * argument.  The workspace is a device array inside the library, one per
+ * device, PROX_STATIC_SCRATCH_BYTES (64 MiB) large and held from the first
+ * call on a device until the process ends; its counters are cleared by a
+ * kernel on `stream` at that first call, and every call leaves them at zero.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Layers whose prox_workspace_size exceeds the limit (e.g. batch 16 at
+ * 4096 x 14336, or batch above 4 at 8192 x 28672) return
+ * PROX_ERR_SCRATCH_LIMIT before touching the device; every batch-1 layer of
+ * the supported shapes fits.  All calls on one device share the array: calls
+ * that may overlap in time on one device (different streams, host threads
+ * without ordering) race and must not be issued.  The stream must belong to
+ * the current device.  Results are bitwise those of prox_ffn_forward_residual
+ * with its own workspace. */
+#define PROX_STATIC_SCRATCH_BYTES (64u << 20)
+prox_status prox_ffn_forward_noalloc(const void *x, int64_t batch, const prox_weights *w,
+                                     const prox_proxy *p, float input_keep, float ffn_sparsity,
+                                     const void *residual, void *out, int32_t *sel_idx_out,
+                                     hipStream_t stream);
 
 /* prox_ffn_forward with timing marks: events[0..5] (host array of six
  * hipEvent_t the caller created) are recorded on the stream before the input

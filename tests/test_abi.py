@@ -172,6 +172,13 @@ def test_other_entry_points_reject(lib):
                                        v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
         assert lib.prox_stage2_exact_ex(v(FAKE), 1, ctypes.byref(w), v(FAKE + 64), 5, ctypes.byref(opt),
                                         v(FAKE + 128), v(FAKE + 256), 1 << 40, None) == B.ERR_UNSUPPORTED
+    # the no-alloc forward refuses, on the host, a layer its static array cannot hold
+    assert lib.prox_ffn_forward_noalloc(v(FAKE), 16, ctypes.byref(_w(8192, 28672)), ctypes.byref(_p(8192, 28672)),
+                                        0.5, 0.7, None, v(FAKE + 20480), None, None) == B.ERR_SCRATCH_LIMIT
+    assert lib.prox_ffn_forward_noalloc(v(FAKE), 1, None, ctypes.byref(_p()), 0.5, 0.7, None, v(FAKE + 20480),
+                                        None, None) == B.ERR_INVALID_ARG
+    assert lib.prox_ffn_forward_noalloc(v(FAKE), 1, ctypes.byref(_w(4100)), ctypes.byref(_p(4100)), 0.5, 0.7, None,
+                                        v(FAKE + 20480), None, None) == B.ERR_UNSUPPORTED
     opt = B._COptions(0, 0, 0, 2)  # an unknown flag
     assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
                                    v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
