@@ -2,14 +2,17 @@
 
 Default workload: one 8B-like FFN layer (d_model 4096, d_ff 14336, bf16
 weights N(0, 0.02^2)), one decode token, input keep 0.5, FFN sparsity 0.7,
-int8 per-row proxy.  A step is one full forward of the layer (both stages,
-five kernels).  Four copies of the weights and proxy (1.9 GB) are cycled so
+int8 per-row proxy.  A step is one full forward of the layer (both stages:
+two kernels for one token).  Four copies of the weights and proxy (1.9 GB) are cycled so
 each step streams its weights from HBM, not from the 256 MB Infinity Cache.
 
 Prints one JSON line: µs per layer (back-to-back steps on one stream), the
-layer's effective GB/s against the 8 TB/s HBM peak, the dominant kernel's
-roofline, the HIP-graph variant, the dense (sparsity 0) comparator, and the
-CPU oracle timed on the host as a baseline.
+layer's effective GB/s against the 8 TB/s HBM peak, per-call latency
+percentiles (one event pair around each call), the dominant kernel's
+roofline beside the measured stream-read ceiling (prox_read_probe over
+1 GiB), the HIP-graph variant, the dense (sparsity 0) comparator, and the
+CPU oracle timed on the host as a baseline (all threads and one thread, the
+dense oracle FFN too, and the CPU model).
 
 The dominant kernel's duration is measured live: a HIP graph of back-to-back
 launches of that kernel alone (cycling the weight sets) is replayed between
@@ -253,22 +256,17 @@ def main():
     us_layer = 1000.0 * ms_total / args.steps
     print("eager %.2f us/layer" % us_layer, file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations, HIP events recorded between the kernels
+    # ---- per-call latency: one event pair around each call, back to back
     n_t = min(args.steps, 200)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_t)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_t)]
     for i in range(n_t):
-        w, p = sets[i % R]
-        P.ffn_forward_timed(x, w, p, keep, sp, evs[i], out=out, workspace=ws)
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
     torch.cuda.synchronize()
-    per = {name: [] for name in P.STEP_NAMES}
-    lat = []
-    for row in evs[n_t // 10:]:
-        for j, name in enumerate(P.STEP_NAMES):
-            per[name].append(1000.0 * row[j].elapsed_time(row[j + 1]))
-        lat.append(1000.0 * row[0].elapsed_time(row[5]))
-    step_us = {n: statistics.mean(v) for n, v in per.items()}
-    lat.sort()
-    latency = dict(median=lat[len(lat) // 2], p10=lat[len(lat) // 10], p90=lat[(9 * len(lat)) // 10])
+    lat = sorted(1000.0 * a.elapsed_time(b) for a, b in evs[n_t // 10:])
+    pick = lambda q: lat[min(len(lat) - 1, int(q * len(lat)))]  # noqa: E731
+    latency = dict(p10=pick(0.10), median=pick(0.50), p90=pick(0.90), p99=pick(0.99), samples=len(lat))
 
     # ---- HIP graph of R forwards (one per weight set), replayed
     graph_us = None
@@ -348,14 +346,33 @@ def main():
     has_s1 = k not in (0, F)
     kern_us = {}
     if has_s1:
-        kern_us["stage1"] = live_us(s1_launch) or (step_us["xselect"] + step_us["proxy"] + step_us["topk"])
-        kern_us["stage2"] = live_us(s2_launch) or (step_us["gateup"] + step_us["down"])
-    else:
-        kern_us["stage2"] = step_us["gateup"] + step_us["down"]
+        kern_us["stage1"] = live_us(s1_launch)
+    kern_us["stage2"] = live_us(s2_launch) if has_s1 else live_us(lambda i: step(i))
+    kern_us = {kk: v for kk, v in kern_us.items() if v is not None}
     kern_bytes = {"stage1": parts["x"] + parts["proxy"] + parts["scales"] + parts["sel"],
                   "stage2": parts["gateup"] + parts["down"] + parts["x"] + parts["out"] + parts["sel"]}
     one_kernel = {"stage1": "stage1_fused_kernel" if (B == 1 and d <= 8192 and F <= 16384) else None,
                   "stage2": "stage2_fused_kernel" if B == 1 else None}
+    # ---- the measured stream-read ceiling: one read of a 1 GiB buffer (four
+    # times the Infinity Cache), the probe kernel's best of several reps
+    read_ceiling = None
+    try:
+        nb = 1 << 30
+        big = torch.empty(nb // 4, dtype=torch.int32, device=dev).fill_(7)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        reps = []
+        for r in range(8):
+            e0.record()
+            P.read_probe(big, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                reps.append(nb / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        read_ceiling = {"gbps": round(max(reps), 1), "median_gbps": round(statistics.median(reps), 1),
+                        "bytes": nb, "kernel": "read_probe_kernel"}
+        del big
+    except Exception as exc:  # pragma: no cover
+        print("read probe unavailable (%r)" % (exc,), file=sys.stderr)
     dom = max(kern_us, key=kern_us.get)
     dom_us, dom_kernel = kern_us[dom], one_kernel[dom]
     dom_bytes = kern_bytes[dom]
@@ -365,7 +382,9 @@ def main():
     traffic = traffic_from_profiles(dom_kernel or dom, wl_name)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom_kernel or dom,
-                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3),
+                "measured_read_ceiling_gbps": None if read_ceiling is None else read_ceiling["gbps"],
+                "frac_of_measured_ceiling": None if read_ceiling is None else round(dom_gbps / read_ceiling["gbps"], 4)}
     layer_gbps = layer_bytes / (us_layer * 1e-6) / 1e9
 
     # ---- dense comparator: the same library at sparsity 0 (Stage 1 skipped)
@@ -475,18 +494,43 @@ def main():
         else:
             f8 = None
             proxy_q = oracle.quantize(wg, mode) + oracle.quantize(wu, mode)
-        times = []
-        deadline = time.time() + 12.0
-        while True:
-            t = time.perf_counter()
-            ref = oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode, fp8=f8)
-            times.append(time.perf_counter() - t)
-            if time.time() > deadline or len(times) >= 40:
-                break
+        def sample(fn, budget_s, max_n):
+            ts = []
+            t_end = time.time() + budget_s
+            while True:
+                t = time.perf_counter()
+                r = fn()
+                ts.append(time.perf_counter() - t)
+                if time.time() > t_end or len(ts) >= max_n:
+                    return r, ts
+        n_all = oracle.get_threads()
+        ref, times = sample(lambda: oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode, fp8=f8), 6.0, 40)
+        _, dense_times = sample(lambda: oracle.ffn_dense(x_host, wg, wu, wd), 4.0, 20)
+        oracle.set_threads(1)
+        try:
+            _, times_1 = sample(lambda: oracle.prox_forward(x_host, wg, wu, wd, proxy_q, keep, sp, mode, fp8=f8),
+                                8.0, 10)
+        finally:
+            oracle.set_threads(n_all)
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for ln in fh:
+                    if ln.startswith("model name"):
+                        cpu_model = ln.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         cpu = {"value": round(1e6 * statistics.median(times), 1), "unit": "us/layer",
-               "cores": oracle.get_threads(), "kind": "oracle",
-               "sample": "%d full oracle forwards of the same layer and token (median), binary64 C loops"
-                         % len(times)}
+               "cores": n_all, "kind": "oracle",
+               "sample": "%d full oracle forwards of the same layer and token (median), binary64 C loops, "
+                         "%d threads" % (len(times), n_all),
+               "value_1_thread": round(1e6 * statistics.median(times_1), 1),
+               "sample_1_thread": "%d forwards on 1 thread (median)" % len(times_1),
+               "dense_oracle_value": round(1e6 * statistics.median(dense_times), 1),
+               "dense_oracle_sample": "%d dense SwiGLU FFNs (all channels, no proxy) on %d threads (median)"
+                                      % (len(dense_times), n_all),
+               "cpu_model": cpu_model, "host_logical_cpus": os.cpu_count()}
         # parity of the timed configuration against the oracle
         sel = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
         y = P.ffn_forward(x, w0, p0, keep, sp, sel_out=sel)
@@ -524,9 +568,9 @@ def main():
         "graph_us_per_layer": None if graph_us is None else round(graph_us, 3),
         "kernels_us": {kk: round(v, 3) for kk, v in kern_us.items()},
         "kernels": {kk: one_kernel[kk] for kk in kern_us},
-        "step_marks_us": {kk: round(v, 3) for kk, v in step_us.items()},
         "kernels_gbps": {kk: round(kern_bytes[kk] / (kern_us[kk] * 1e-6) / 1e9, 1) for kk in kern_us},
         "roofline": roofline,
+        "hbm_read_ceiling": read_ceiling,
         "dense_us_per_layer": None if dense_us is None else round(dense_us, 3),
         "cpu_baseline": cpu,
         "parity": parity,

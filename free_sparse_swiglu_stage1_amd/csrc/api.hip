@@ -588,6 +588,13 @@ prox_status prox_workspace_init(void *workspace, size_t workspace_bytes, hipStre
     return hip_status(launch_zero_u32((uint32_t *)workspace, kZeroWords, stream));
 }
 
+prox_status prox_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (bad_ptr(buf) || !sink || ((uintptr_t)sink & 3u)) return PROX_ERR_INVALID_ARG;
+    if (bytes == 0 || bytes % 16 != 0) return PROX_ERR_INVALID_ARG;
+    return hip_status(launch_read_probe(buf, bytes, sink, stream));
+}
+
 prox_status prox_workspace_check(const void *workspace, size_t workspace_bytes, uint32_t *fallbacks,
                                  hipStream_t stream)
 {

@@ -179,6 +179,9 @@ hipError_t launch_layer(const void *x, int d, int F, int k_in, int k, const uint
 // hold one of its 1024-thread workgroups).
 int layer_groups();
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t st);
+// Stream-read probe (probe.hip): reads bytes/16 16-byte vectors, XORs every
+// 32-bit word read into *sink (device-scope atomics).
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
 hipError_t launch_pack(int dtype, const void *w_gate, const void *w_up, const void *w_down, int d, int F,
                        void *w_gu, void *w_down_t, hipStream_t st);

@@ -33,7 +33,7 @@ SYMBOLS = (
     "prox_quantize_proxy", "prox_workspace_size", "prox_workspace_init", "prox_ffn_forward", "prox_ffn_forward_residual",
     "prox_ffn_forward_timed", "prox_stage1_select", "prox_topk", "prox_stage2_exact", "prox_rmsnorm", "prox_chain_forward",
     "prox_ffn_forward_ex", "prox_stage2_exact_ex", "prox_effective_sparsity", "prox_allocate_sparsity",
-    "prox_workspace_check", "prox_ffn_forward_noalloc",
+    "prox_workspace_check", "prox_ffn_forward_noalloc", "prox_read_probe",
 )
 
 
@@ -111,6 +111,7 @@ def load_library(path: str = LIB_PATH):
         "prox_effective_sparsity": ([PM, D, D, PD], I32),
         "prox_allocate_sparsity": ([PM, D, D, D, PD, PD], I32),
         "prox_ffn_forward_noalloc": ([P, I64, PW, PP, F, F, P, P, P, P], I32),
+        "prox_read_probe": ([P, ctypes.c_size_t, P, P], I32),
     }
     for name in SYMBOLS:
         fn = getattr(lib, name)
@@ -357,6 +358,15 @@ def ffn_forward_noalloc(x: torch.Tensor, w: Weights, p: Proxy, input_keep: float
                                       ffn_sparsity, _ptr(residual), _ptr(out), _ptr(sel_out), _stream(x.device))
     _check(st, "prox_ffn_forward_noalloc")
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """XOR of every 32-bit word of buf (its bytes a multiple of 16) into
+    sink[0] (int32, device): one stream read of buf, for timing."""
+    lib = load_library()
+    _dev(buf, "buf")
+    _check(lib.prox_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf.device)),
+           "prox_read_probe")
 
 
 STEP_NAMES = ("xselect", "proxy", "topk", "gateup", "down")

@@ -154,6 +154,16 @@ prox_status prox_effective_sparsity(const prox_cost_model *m, double input_keep,
 prox_status prox_allocate_sparsity(const prox_cost_model *m, double target_effective, double s2_anchor,
                                    double min_keep, double *input_keep_out, double *ffn_sparsity_out);
 
+/* Measurement aid, not part of the method: reads `bytes` (a multiple of 16)
+ * of device memory at buf (16-byte aligned) once, in 16-byte non-temporal
+ * loads spread over the whole device, and XORs every 32-bit word read into
+ * *sink (device, caller-initialized; the result is the XOR of the buffer's
+ * words, so the read is checkable).  Timed over a buffer far larger than the
+ * 256 MB Infinity Cache, it gives the sustained HBM read rate the forward's
+ * kernels are compared with, beside the nominal peak.  Bad pointers or sizes:
+ * PROX_ERR_INVALID_ARG. */
+prox_status prox_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *prox_status_string(int status);
 

@@ -179,6 +179,11 @@ def test_other_entry_points_reject(lib):
                                         None, None) == B.ERR_INVALID_ARG
     assert lib.prox_ffn_forward_noalloc(v(FAKE), 1, ctypes.byref(_w(4100)), ctypes.byref(_p(4100)), 0.5, 0.7, None,
                                         v(FAKE + 20480), None, None) == B.ERR_UNSUPPORTED
+    sink = v(FAKE + 64)
+    assert lib.prox_read_probe(None, 1024, sink, None) == B.ERR_INVALID_ARG
+    assert lib.prox_read_probe(v(FAKE), 1000, sink, None) == B.ERR_INVALID_ARG  # not whole 16-byte vectors
+    assert lib.prox_read_probe(v(FAKE), 0, sink, None) == B.ERR_INVALID_ARG
+    assert lib.prox_read_probe(v(FAKE), 1024, None, None) == B.ERR_INVALID_ARG
     opt = B._COptions(0, 0, 0, 2)  # an unknown flag
     assert lib.prox_ffn_forward_ex(v(FAKE), 1, ctypes.byref(w), ctypes.byref(p), 0.5, 0.7, ctypes.byref(opt), None,
                                    v(FAKE + 20480), None, v(FAKE + 32768), 1 << 40, None) == B.ERR_UNSUPPORTED
