@@ -96,9 +96,9 @@ def algorithmic_bytes(d, F, B, k, k_union, bw, mode, fp8=False):
                 down=k * d * ww + (4 * d if fp8 and k else 0), sel=k * 4, out=B * d * bw)
 
 
-# the sources the single-token kernels (stage1_fused_kernel, stage2_fused_kernel)
+# the sources the single-token kernels (stage1_fused_kernel, stage2_rows_kernel, stage2_fused_kernel)
 # are built from: the stored counter traffic is valid while these are unchanged
-DIGEST_SOURCES = ("common.h", "kernels.h", "select.h", "stage1_fused.hip", "stage2.hip")
+DIGEST_SOURCES = ("common.h", "kernels.h", "select.h", "stage1_fused.hip", "stage2.hip", "stage2_rows.hip")
 
 
 def source_digest() -> str:
@@ -351,8 +351,9 @@ def main():
     kern_us = {kk: v for kk, v in kern_us.items() if v is not None}
     kern_bytes = {"stage1": parts["x"] + parts["proxy"] + parts["scales"] + parts["sel"],
                   "stage2": parts["gateup"] + parts["down"] + parts["x"] + parts["out"] + parts["sel"]}
+    rows = B == 1 and dtype == "bf16" and not fp8 and d in (4096, 8192) and -(-k // 256) <= 128
     one_kernel = {"stage1": "stage1_fused_kernel" if (B == 1 and d <= 8192 and F <= 16384) else None,
-                  "stage2": "stage2_fused_kernel" if B == 1 else None}
+                  "stage2": ("stage2_rows_kernel" if rows else "stage2_fused_kernel") if B == 1 else None}
     # ---- the measured stream-read ceiling: one read of a 1 GiB buffer (four
     # times the Infinity Cache), the probe kernel's best of several reps
     read_ceiling = None

@@ -27,10 +27,13 @@ constexpr int kMaxBatchInt4 = 4;
 // The workspace starts with counters that must be zero between calls:
 // [0,511) proxy channel blocks, 511 the single-token Stage 1's score ticket,
 // [512,1023) down slices, [1024,1535) the single-token Stage 2's finished
-// slice tails, [1536,2047) its slice-tail claims, 2047 the count of bounded
-// waits that gave up (never reset by a call), then from 4096 the
-// single-token Stage 2's per-split lines (64 pages of 4 KB).  Each other word
-// is reset by the last workgroup to use it.
+// slice tails, [1536,2047) its slice-tail claims, 2045 and [2048,3072) the
+// single-launch layer's barriers, 2046 its failed waits and 2047 the count
+// of bounded waits that gave up (neither reset by a call), then from 4096
+// the single-token Stage 2's per-split lines (64 pages of 4 KB).  Each other
+// word is reset by the last workgroup to use it, except the rows Stage 2's
+// arrival count (3072, 64 bits) and release lines (lines 1024.. of the
+// per-split pages), which hold launch numbers.
 constexpr int kCounters = kS2SyncBase + kS2SyncWords;
 constexpr int kZeroWords = kCounters;
 // The channel-block and slice ticket words: the batched Stage 1 clears them
@@ -193,7 +196,7 @@ struct Workspace {
     uint32_t *counters;
     float *lk_part;   // single-launch layer: proxy block partials
     uint32_t *lk_selw; // single-launch layer: the published selection
-    float *lk_ypart;  // single-launch layer: per-workgroup partial outputs
+    float *ypart;     // one token's per-workgroup partial outputs (rows Stage 2, single-launch layer)
     float *xh;
     float *proxy_part;
     float *score;
@@ -238,13 +241,14 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
         w.s_pieces = nullptr;
         w.bdn_part = nullptr;
     }
-    if (B == 1 && (d == 4096 || d == 8192) && F <= kFusedMaxF) {  // the single-launch layer
-        w.lk_part = (float *)take(sizeof(float) * (size_t)kLayerMaxGroups * 2048);
-        w.lk_selw = (uint32_t *)take(sizeof(uint32_t) * 1024);  // the published selection
-        w.lk_ypart = (float *)take(sizeof(float) * (size_t)kLayerMaxGroups * d);
-    } else {
-        w.lk_part = w.lk_ypart = nullptr;
-        w.lk_selw = nullptr;
+    w.lk_part = w.ypart = nullptr;
+    w.lk_selw = nullptr;
+    if (B == 1 && (d == 4096 || d == 8192)) {  // the rows Stage 2 and the single-launch layer
+        w.ypart = (float *)take(sizeof(float) * (size_t)kRowsMaxGroups * d);
+        if (F <= kFusedMaxF) {
+            w.lk_part = (float *)take(sizeof(float) * (size_t)kLayerMaxGroups * 2048);
+            w.lk_selw = (uint32_t *)take(sizeof(uint32_t) * 1024);  // the published selection
+        }
     }
     w.bytes = off;
     return w;
@@ -267,7 +271,7 @@ prox_status run_layer(const void *x, const prox_weights *w, const prox_proxy *p,
 {
     return hip_status(launch_layer(x, (int)w->d_model, (int)w->d_ff, (int)k_in, (int)k, (const uint8_t *)p->codes,
                                    (const float *)p->scales, w->w_gu, w->w_down_t, residual, out, sel_out, ws.lk_part,
-                                   ws.score, ws.lk_selw, ws.lk_ypart, ws.counters, o.act, o.signal, o.spin_ticks,
+                                   ws.score, ws.lk_selw, ws.ypart, ws.counters, o.act, o.signal, o.spin_ticks,
                                    G, st));
 }
 
@@ -330,6 +334,15 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         TRY_HIP(launch_fill_out(dt, (int)B, (int)d, residual, out, st));
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
+    }
+    if (B == 1 && dt == 1 && sw.fmt == 0 && ws.ypart) {  // bf16: one workgroup per CU streams whole channels
+        const int G = rows_groups();
+        if (G && rows_supported(d, w->d_ff, k, G)) {
+            TRY_HIP(launch_stage2_rows(x, (int)d, (int)w->d_ff, sel, (int)k, sw.w_gu, sw.w_down_t, residual, out,
+                                       iota_out, ws.ypart, ws.counters, sw.act, o.spin_ticks, G, st));
+            TRY_HIP(mark(ev, 4, st));
+            return hip_status(mark(ev, 5, st));
+        }
     }
     if (B == 1) {  // one launch: the down projection starts while gate/up drains
         TRY_HIP(launch_stage2_fused(dt, sw, x, (int)d, (int)w->d_ff, sel, (int)k, ws.s_sp, ws.down_part, residual,
@@ -608,7 +621,14 @@ prox_status prox_workspace_check(const void *workspace, size_t workspace_bytes, 
         free(h);
         return PROX_ERR_HIP;
     }
+    // the rows Stage 2's words hold launch numbers: its arrival count must be
+    // a whole number of launches
     bool clean = true;
+    for (int i = 0; i < kRowsMaxGroups; ++i) h[s2_sync_line(kRowsReleaseBase + i)] = 0u;
+    const uint64_t arrivals = (uint64_t)h[kRowsArriveSlot] | ((uint64_t)h[kRowsArriveSlot + 1] << 32);
+    h[kRowsArriveSlot] = h[kRowsArriveSlot + 1] = 0u;
+    const int G = arrivals ? rows_groups() : 0;
+    if (arrivals && (G == 0 || arrivals % (uint64_t)G != 0)) clean = false;
     for (int i = 0; i < kZeroWords; ++i)
         if (i != kFallbackSlot && i != kLayerErrorSlot && h[i] != 0u) clean = false;
     *fallbacks = h[kFallbackSlot];

@@ -1,7 +1,8 @@
 // Stream-read probe: the device's sustained HBM read rate, against which the
 // forward's kernels are compared beside the 8 TB/s nominal peak.  Every
 // thread reads 16-byte vectors grid-stride with non-temporal loads (no reuse,
-// as the forward's weight streams) and folds them with XOR; each thread adds
+// as the forward's weight streams), so that at each step the grid reads one
+// contiguous 8 MB stretch, and folds them with XOR; each thread adds
 // its fold to one word with a device-scope atomic XOR, so the result is
 // checkable (the XOR of every 32-bit word read) and the loads cannot be
 // optimized away.
@@ -20,16 +21,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4 *
 {
     uint32_t acc = 0u;
     const size_t stride = (size_t)gridDim.x * kProbeThreads;
-    size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
-    // four vectors in flight per thread
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
-    }
-    for (; i < n; i += stride) {
+    for (size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n; i += stride) {
         const u32x4 v = __builtin_nontemporal_load(p + i);
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }

@@ -1,0 +1,368 @@
+// Stage 2 of Prox for one bf16 token with bf16 weights ("Stage 2: Exact
+// Sparse Computation"): on the selected channels only, g = W_gate x,
+// u = W_up x, s = act(g) u and y = sum_j s_j W_down[:, j], for d_model 4096
+// or 8192.
+//
+// One 1024-thread workgroup per CU.  Workgroup w takes the selected channels
+// of rank [wk/G, (w+1)k/G) and streams all three rows of each: the gate and
+// up rows give s_j, which scales the down row into a partial y of d columns
+// held in registers.  No workgroup waits for another before its partial is
+// stored, so the gate/up -> down dependency never crosses workgroups.
+//  - The two halves of the workgroup take alternate channels; thread t of a
+//    half holds columns [t CPT, (t+1) CPT) of its channels' rows (16-byte
+//    loads).  A round's rows are requested together and the next round's
+//    before the current one is reduced; g and u are added over lanes and
+//    the half's eight waves in a fixed order.  The halves' partials are added
+//    (first + second) and stored with device-coherent 16-byte stores.
+//  - The end: each workgroup takes an arrival ticket.  The last R arrivals
+//    (R = min(G, d / 32)) each add up 32-column slices of y over the G
+//    partials in a fixed order (32 groups of every 32nd partial, then the
+//    groups in order), add the residual and round.  The very last arrival
+//    releases the other R - 1 by writing the launch's number into each one's
+//    release word (128-byte lines 4 KB apart, so the polls spread over the
+//    memory channels).
+// Every sum runs in a fixed order: the result is bitwise deterministic and
+// independent of which workgroup adds which slice.
+//
+// Waits are bounded.  The arrival count is a 64-bit count that only grows
+// (launch e's arrivals are the tickets e G .. e G + G - 1) and the release
+// words hold launch numbers, so nothing is reset and a wait that gives up
+// leaves no state behind for the next launch.  A workgroup whose wait gives
+// up computes every workgroup's partial itself -- bitwise the value that
+// workgroup stores -- stores it, and goes on: the result is the same, only
+// later, and the give-up is counted in the fallback slot.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace prox {
+
+constexpr int kRT = 1024;         // threads per workgroup
+constexpr int kRW = kRT / 64;     // waves
+constexpr int kRSumGroups = 32;   // partial groups of a slice sum
+constexpr int kRSliceCols = 32;   // columns of a slice
+
+struct RowsArgs {
+    const uint16_t *x;         // [d] bf16
+    const uint16_t *w_gu;      // [F][2][d]
+    const uint16_t *w_dt;      // [F][d]
+    const int32_t *sel;        // [k] ascending, or null: channel r at rank r
+    const uint16_t *residual;  // [d] or null (may alias out)
+    uint16_t *out;             // [d]
+    int32_t *iota_out;         // [k] or null: the ranks' channels are written (sel null only)
+    float *ypart;              // [G][d]
+    uint32_t *counters;
+    uint64_t spin_ticks;
+    int d, F, k, G, act;
+};
+
+template <int KX>
+struct alignas(16) RowsSmem {
+    static constexpr int CPT = 2 * KX;   // columns per thread (one half covers a row)
+    static constexpr int RC = 24 / CPT;  // channels per half and round
+    union {
+        struct {
+            float r2[kRW][2 * RC];
+            float sv[2][RC];
+        } e;
+        float yhalf[kRT / 2][CPT + 1];   // the second half's sums (padded: no bank conflicts)
+        float sums[kRSumGroups][kRSliceCols];
+    } u;
+    int chan[kRowsMaxChan];
+    int flag;
+    uint32_t epoch;
+    int pos;
+};
+
+__device__ __forceinline__ u32x4 rows_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
+}
+
+// Workgroup v's partial y over its ranks, stored to ypart[v]: all threads
+// call; the value depends on v and the inputs only.
+template <int KX>
+__device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const float (&xs)[2 * KX])
+{
+    constexpr int CPT = RowsSmem<KX>::CPT;
+    constexpr int NV = CPT / 8;  // 16-byte vectors per row and thread
+    constexpr int RC = RowsSmem<KX>::RC;
+    const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+    const int half = uniform(tid >> 9), ht = tid & 511;
+    const int d = a.d, F = a.F;
+    const int r0 = (int)((int64_t)v * a.k / a.G), r1 = (int)((int64_t)(v + 1) * a.k / a.G);
+    const int nc = r1 - r0;
+    __syncthreads();  // the previous user of the channel list and the LDS is done
+    if (tid < nc) sm.chan[tid] = a.sel ? min(max(a.sel[r0 + tid], 0), F - 1) : r0 + tid;  // clamped into [0, F)
+    __syncthreads();
+
+    float yacc[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) yacc[q] = 0.0f;
+    const uint32_t rowb = 2u * (uint32_t)d;  // bytes of a row
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.w_gu), (short)0, (int)(2u * rowb * (uint32_t)F), CoherentBuf::kWord3);
+    const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.w_dt), (short)0, (int)(rowb * (uint32_t)F), CoherentBuf::kWord3);
+    const uint32_t goob = 2u * rowb * (uint32_t)F, doob = rowb * (uint32_t)F;
+    const uint32_t coff = (uint32_t)(ht * CPT * 2);
+    u32x4 ag[RC][NV], au[RC][NV], ad[RC][NV], bg[RC][NV], bu[RC][NV], bd[RC][NV];
+    // a round's rows: list entries (rd RC + c) 2 + half; past the list the
+    // offsets are out of range and read zero without touching memory
+    auto issue = [&](u32x4(&vg)[RC][NV], u32x4(&vu)[RC][NV], u32x4(&vd)[RC][NV], int rd) {
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const int i = (rd * RC + c) * 2 + half;
+            const bool live = i < nc;
+            const uint32_t j = (uint32_t)sm.chan[live ? i : 0];
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                vg[c][q] = rows_ld16(grs, live ? j * 2u * rowb + coff + 16u * q : goob);
+                vu[c][q] = rows_ld16(grs, live ? j * 2u * rowb + rowb + coff + 16u * q : goob);
+                vd[c][q] = rows_ld16(drs, live ? j * rowb + coff + 16u * q : doob);
+            }
+        }
+    };
+    auto process = [&](const u32x4(&vg)[RC][NV], const u32x4(&vu)[RC][NV], const u32x4(&vd)[RC][NV], int rd) {
+        float pg[RC], pu[RC];
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            float g = 0.0f, u = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                float fg[8], fu[8];
+                vec16<uint16_t>::unpack(vg[c][q], fg);
+                vec16<uint16_t>::unpack(vu[c][q], fu);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    g = fmaf(fg[e], xs[8 * q + e], g);
+                    u = fmaf(fu[e], xs[8 * q + e], u);
+                }
+            }
+            pg[c] = wave_sum(g);
+            pu[c] = wave_sum(u);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                sm.u.e.r2[wv][c] = pg[c];
+                sm.u.e.r2[wv][RC + c] = pu[c];
+            }
+        }
+        __syncthreads();
+        if (tid < 2 * RC) {  // channel c of half h: that half's eight waves in order
+            const int h = tid / RC, c = tid % RC;
+            float tg[kRW / 2], tu[kRW / 2];
+#pragma unroll
+            for (int ww = 0; ww < kRW / 2; ++ww) {
+                tg[ww] = sm.u.e.r2[8 * h + ww][c];
+                tu[ww] = sm.u.e.r2[8 * h + ww][RC + c];
+            }
+            float g = tg[0], u = tu[0];
+#pragma unroll
+            for (int ww = 1; ww < kRW / 2; ++ww) {
+                g += tg[ww];
+                u += tu[ww];
+            }
+            sm.u.e.sv[h][c] = ((rd * RC + c) * 2 + h < nc) ? gate_act(a.act, g) * u : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const float sv = sm.u.e.sv[half][c];
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                float fd[8];
+                vec16<uint16_t>::unpack(vd[c][q], fd);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) yacc[8 * q + e] = fmaf(sv, fd[e], yacc[8 * q + e]);
+            }
+        }
+    };
+    const int nr = (nc + 2 * RC - 1) / (2 * RC);
+    if (nr > 0) issue(ag, au, ad, 0);
+    for (int rd = 0; rd < nr; rd += 2) {
+        issue(bg, bu, bd, rd + 1);
+        process(ag, au, ad, rd);
+        if (rd + 1 < nr) {
+            issue(ag, au, ad, rd + 2);
+            process(bg, bu, bd, rd + 1);
+        }
+    }
+    // the halves' sums added (first half + second half) and stored
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) sm.u.yhalf[ht][q] = yacc[q];
+    }
+    __syncthreads();
+    if (half == 0) {  // 16-byte device-coherent stores
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+            a.ypart + (int64_t)v * d, (short)0, (int)(sizeof(float) * d), CoherentBuf::kWord3);
+#pragma unroll
+        for (int q = 0; q < CPT; q += 4) {
+            u32x4 val;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = __float_as_uint(yacc[q + e] + sm.u.yhalf[ht][q + e]);
+            __builtin_amdgcn_raw_buffer_store_b128(val, yrs, (int)(sizeof(float) * (ht * CPT + q)), 0,
+                                                   CoherentBuf::kSc1);
+        }
+    }
+}
+
+template <int KX>
+__global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
+{
+    constexpr int CPT = RowsSmem<KX>::CPT;
+    constexpr int NV = CPT / 8;
+    __shared__ RowsSmem<KX> sm;
+    const int tid = threadIdx.x, w = blockIdx.x, G = a.G, d = a.d;
+    const int ht = tid & 511;
+    float xs[CPT];
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+        vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4 *>(a.x + ht * CPT + 8 * q), xs + 8 * q);
+    rows_partial<KX>(a, w, sm, xs);
+    if (a.iota_out && !a.sel) {
+        const int r0 = (int)((int64_t)w * a.k / G), r1 = (int)((int64_t)(w + 1) * a.k / G);
+        if (tid < r1 - r0) a.iota_out[r0 + tid] = r0 + tid;
+    }
+
+    // ---- arrival: the last R arrivals add up the slices
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t *arrive = reinterpret_cast<uint64_t *>(&a.counters[kRowsArriveSlot]);
+        const uint64_t t = __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.pos = (int)(t % (uint64_t)G);
+        sm.epoch = (uint32_t)(t / (uint64_t)G) + 1u;
+    }
+    __syncthreads();
+    const int pos = sm.pos;
+    const uint32_t epoch = sm.epoch;
+    const int n_chunks = d / kRSliceCols;
+    const int R = G < n_chunks ? G : n_chunks;
+    if (pos < G - R) return;
+    const int s = pos - (G - R);
+    if (pos == G - 1) {  // every partial is stored: release the other slice workgroups
+        for (int i = tid; i < R - 1; i += kRT)
+            __hip_atomic_store(&a.counters[s2_sync_line(kRowsReleaseBase + i)], epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        if (tid == 0) {
+            const uint32_t *rel = &a.counters[s2_sync_line(kRowsReleaseBase + s)];
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            bool ok = true;
+            while ((int32_t)(__hip_atomic_load(const_cast<uint32_t *>(rel), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
+                __builtin_amdgcn_s_sleep(1);
+                if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin_ticks) {
+                    ok = false;
+                    break;
+                }
+            }
+            if (!ok) __hip_atomic_fetch_add(&a.counters[kFallbackSlot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm.flag = ok;
+        }
+        __syncthreads();
+        if (!sm.flag) {  // gave up: every partial computed here, bitwise as its workgroup stores it
+            for (int v = 0; v < G; ++v) rows_partial<KX>(a, v, sm, xs);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+    }
+    __syncthreads();
+
+    // ---- slices s, s + R, ...: 32 columns each over the G partials
+    const CoherentBuf ybuf(a.ypart, (uint32_t)(sizeof(float) * G * d));
+    const uint32_t yend = (uint32_t)(sizeof(float) * G * d);
+    const int col = tid & (kRSliceCols - 1), grp = tid >> 5;  // grp: partials grp, grp + 32, ...
+    for (int ch = s; ch < n_chunks; ch += R) {
+        const int cA = ch * kRSliceCols;
+        float v = 0.0f;
+        for (int p0 = grp; p0 < G; p0 += kRSumGroups * 8) {
+            float t8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int p = p0 + kRSumGroups * i;
+                t8[i] = ybuf.load(p < G ? (uint32_t)(sizeof(float) * ((int64_t)p * d + cA + col)) : yend);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (p0 + kRSumGroups * i < G) v += t8[i];
+        }
+        sm.u.sums[grp][col] = v;
+        __syncthreads();
+        if (tid < kRSliceCols) {
+            float t[kRSumGroups];
+#pragma unroll
+            for (int g = 0; g < kRSumGroups; ++g) t[g] = sm.u.sums[g][tid];
+            float y = t[0];
+#pragma unroll
+            for (int g = 1; g < kRSumGroups; ++g) y += t[g];
+            if (a.residual) y += __uint_as_float((uint32_t)a.residual[cA + tid] << 16);
+            a.out[cA + tid] = f32_to_bf16(y);
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------
+bool rows_supported(int64_t d, int64_t F, int64_t k, int G)
+{
+    if ((d != 4096 && d != 8192) || F < 16 || k <= 0 || k > F) return false;
+    if (G < kRSumGroups || G > kRowsMaxGroups) return false;
+    return (k + G - 1) / G <= kRowsMaxChan;
+}
+
+hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, int k, const void *w_gu,
+                              const void *w_dt, const void *residual, void *out, int32_t *iota_out, float *ypart,
+                              uint32_t *counters, int act, uint64_t spin_ticks, int G, hipStream_t st)
+{
+    if (!rows_supported(d, F, k, G)) return hipErrorInvalidValue;
+    RowsArgs a;
+    a.x = (const uint16_t *)x;
+    a.w_gu = (const uint16_t *)w_gu;
+    a.w_dt = (const uint16_t *)w_dt;
+    a.sel = sel;
+    a.residual = (const uint16_t *)residual;
+    a.out = (uint16_t *)out;
+    a.iota_out = iota_out;
+    a.ypart = ypart;
+    a.counters = counters;
+    a.spin_ticks = spin_ticks ? spin_ticks : kDefaultSpinTicks;
+    a.d = d;
+    a.F = F;
+    a.k = k;
+    a.G = G;
+    a.act = act;
+    if (d == 4096) stage2_rows_kernel<4><<<G, kRT, 0, st>>>(a);
+    else stage2_rows_kernel<8><<<G, kRT, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+int rows_groups()
+{
+    constexpr int kMaxDevices = 64;
+    static int cache[kMaxDevices];  // groups + 1 per device; 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    const int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (c) return c - 1;
+    int cus = 0, g = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+        const void *fns[] = {(const void *)stage2_rows_kernel<4>, (const void *)stage2_rows_kernel<8>};
+        int occ = 1 << 30;
+        for (const void *f : fns) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kRT, 0) != hipSuccess) n = 0;
+            occ = n < occ ? n : occ;
+        }
+        if (occ >= 1) g = cus < kRowsMaxGroups ? cus : kRowsMaxGroups;
+    }
+    (void)hipGetLastError();  // a failed query leaves no error for the next call to report
+    __atomic_store_n(&cache[dev], g + 1, __ATOMIC_RELAXED);
+    return g;
+}
+
+}  // namespace prox
