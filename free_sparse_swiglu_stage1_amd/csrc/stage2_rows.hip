@@ -8,12 +8,14 @@
 // up rows give s_j, which scales the down row into a partial y of d columns
 // held in registers.  No workgroup waits for another before its partial is
 // stored, so the gate/up -> down dependency never crosses workgroups.
-//  - The two halves of the workgroup take alternate channels; thread t of a
-//    half holds columns [t CPT, (t+1) CPT) of its channels' rows (16-byte
-//    loads).  A round's rows are requested together and the next round's
-//    before the current one is reduced; g and u are added over lanes and
-//    the half's eight waves in a fixed order.  The halves' partials are added
-//    (first + second) and stored with device-coherent 16-byte stores.
+//  - A row is covered by a group of d / 8 threads, thread t holding columns
+//    [8t, 8t + 8) (one 16-byte load per row): at d_model 4096 the two halves
+//    of the workgroup are two groups and take alternate channels, at 8192
+//    the whole workgroup is one group.  Each group takes 3 channels a round;
+//    a round's rows are requested together and the next round's before the
+//    current one is reduced; g and u are added over lanes and the group's
+//    waves in a fixed order.  The groups' partials are added (first +
+//    second) and stored with device-coherent 16-byte stores.
 //  - The end: each workgroup takes an arrival ticket.  The last R arrivals
 //    (R = min(G, d / 32)) each add up 32-column slices of y over the G
 //    partials in a fixed order (32 groups of every 32nd partial, then the
@@ -57,16 +59,17 @@ struct RowsArgs {
     int d, F, k, G, act;
 };
 
-template <int KX>
+// H: channel groups of the workgroup (2 at d_model 4096, 1 at 8192)
+template <int H>
 struct alignas(16) RowsSmem {
-    static constexpr int CPT = 2 * KX;   // columns per thread (one half covers a row)
-    static constexpr int RC = 24 / CPT;  // channels per half and round
+    static constexpr int CPT = 8;   // columns per thread: a group of kRT / H threads covers a row
+    static constexpr int RC = 3;    // channels per group and round
     union {
         struct {
             float r2[kRW][2 * RC];
-            float sv[2][RC];
+            float sv[H][RC];
         } e;
-        float yhalf[kRT / 2][CPT + 1];   // the second half's sums (padded: no bank conflicts)
+        float yhalf[kRT / 2][CPT + 1];   // H = 2: the second group's sums (padded: no bank conflicts)
         float sums[kRSumGroups][kRSliceCols];
     } u;
     int chan[kRowsMaxChan];
@@ -82,14 +85,15 @@ __device__ __forceinline__ u32x4 rows_ld16(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // Workgroup v's partial y over its ranks, stored to ypart[v]: all threads
 // call; the value depends on v and the inputs only.
-template <int KX>
-__device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const float (&xs)[2 * KX])
+template <int H>
+__device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H> &sm, const float (&xs)[8])
 {
-    constexpr int CPT = RowsSmem<KX>::CPT;
+    constexpr int CPT = RowsSmem<H>::CPT;
     constexpr int NV = CPT / 8;  // 16-byte vectors per row and thread
-    constexpr int RC = RowsSmem<KX>::RC;
+    constexpr int RC = RowsSmem<H>::RC;
+    constexpr int GT = kRT / H, GW = kRW / H;  // threads and waves of a group
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
-    const int half = uniform(tid >> 9), ht = tid & 511;
+    const int grp = uniform(tid / GT), ht = tid % GT;
     const int d = a.d, F = a.F;
     const int r0 = (int)((int64_t)v * a.k / a.G), r1 = (int)((int64_t)(v + 1) * a.k / a.G);
     const int nc = r1 - r0;
@@ -108,12 +112,12 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const f
     const uint32_t goob = 2u * rowb * (uint32_t)F, doob = rowb * (uint32_t)F;
     const uint32_t coff = (uint32_t)(ht * CPT * 2);
     u32x4 ag[RC][NV], au[RC][NV], ad[RC][NV], bg[RC][NV], bu[RC][NV], bd[RC][NV];
-    // a round's rows: list entries (rd RC + c) 2 + half; past the list the
+    // a round's rows: list entries (rd RC + c) H + grp; past the list the
     // offsets are out of range and read zero without touching memory
     auto issue = [&](u32x4(&vg)[RC][NV], u32x4(&vu)[RC][NV], u32x4(&vd)[RC][NV], int rd) {
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
-            const int i = (rd * RC + c) * 2 + half;
+            const int i = (rd * RC + c) * H + grp;
             const bool live = i < nc;
             const uint32_t j = (uint32_t)sm.chan[live ? i : 0];
 #pragma unroll
@@ -151,26 +155,26 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const f
             }
         }
         __syncthreads();
-        if (tid < 2 * RC) {  // channel c of half h: that half's eight waves in order
+        if (tid < H * RC) {  // channel c of group h: that group's waves in order
             const int h = tid / RC, c = tid % RC;
-            float tg[kRW / 2], tu[kRW / 2];
+            float tg[GW], tu[GW];
 #pragma unroll
-            for (int ww = 0; ww < kRW / 2; ++ww) {
-                tg[ww] = sm.u.e.r2[8 * h + ww][c];
-                tu[ww] = sm.u.e.r2[8 * h + ww][RC + c];
+            for (int ww = 0; ww < GW; ++ww) {
+                tg[ww] = sm.u.e.r2[GW * h + ww][c];
+                tu[ww] = sm.u.e.r2[GW * h + ww][RC + c];
             }
             float g = tg[0], u = tu[0];
 #pragma unroll
-            for (int ww = 1; ww < kRW / 2; ++ww) {
+            for (int ww = 1; ww < GW; ++ww) {
                 g += tg[ww];
                 u += tu[ww];
             }
-            sm.u.e.sv[h][c] = ((rd * RC + c) * 2 + h < nc) ? gate_act(a.act, g) * u : 0.0f;
+            sm.u.e.sv[h][c] = ((rd * RC + c) * H + h < nc) ? gate_act(a.act, g) * u : 0.0f;
         }
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
-            const float sv = sm.u.e.sv[half][c];
+            const float sv = sm.u.e.sv[grp][c];
 #pragma unroll
             for (int q = 0; q < NV; ++q) {
                 float fd[8];
@@ -180,7 +184,7 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const f
             }
         }
     };
-    const int nr = (nc + 2 * RC - 1) / (2 * RC);
+    const int nr = (nc + H * RC - 1) / (H * RC);
     if (nr > 0) issue(ag, au, ad, 0);
     for (int rd = 0; rd < nr; rd += 2) {
         issue(bg, bu, bd, rd + 1);
@@ -190,40 +194,37 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<KX> &sm, const f
             process(bg, bu, bd, rd + 1);
         }
     }
-    // the halves' sums added (first half + second half) and stored
+    // the groups' sums added (first group + second group) and stored
     __syncthreads();
-    if (half == 1) {
+    if (H == 2 && grp == 1) {
 #pragma unroll
         for (int q = 0; q < CPT; ++q) sm.u.yhalf[ht][q] = yacc[q];
     }
     __syncthreads();
-    if (half == 0) {  // 16-byte device-coherent stores
+    if (grp == 0) {  // 16-byte device-coherent stores
         const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
             a.ypart + (int64_t)v * d, (short)0, (int)(sizeof(float) * d), CoherentBuf::kWord3);
 #pragma unroll
         for (int q = 0; q < CPT; q += 4) {
             u32x4 val;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) val[e] = __float_as_uint(yacc[q + e] + sm.u.yhalf[ht][q + e]);
+            for (int e = 0; e < 4; ++e)
+                val[e] = __float_as_uint(H == 2 ? yacc[q + e] + sm.u.yhalf[ht][q + e] : yacc[q + e]);
             __builtin_amdgcn_raw_buffer_store_b128(val, yrs, (int)(sizeof(float) * (ht * CPT + q)), 0,
                                                    CoherentBuf::kSc1);
         }
     }
 }
 
-template <int KX>
+template <int H>
 __global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
 {
-    constexpr int CPT = RowsSmem<KX>::CPT;
-    constexpr int NV = CPT / 8;
-    __shared__ RowsSmem<KX> sm;
+    __shared__ RowsSmem<H> sm;
     const int tid = threadIdx.x, w = blockIdx.x, G = a.G, d = a.d;
-    const int ht = tid & 511;
-    float xs[CPT];
-#pragma unroll
-    for (int q = 0; q < NV; ++q)
-        vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4 *>(a.x + ht * CPT + 8 * q), xs + 8 * q);
-    rows_partial<KX>(a, w, sm, xs);
+    const int ht = tid % (kRT / H);
+    float xs[8];
+    vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4 *>(a.x + 8 * ht), xs);
+    rows_partial<H>(a, w, sm, xs);
     if (a.iota_out && !a.sel) {
         const int r0 = (int)((int64_t)w * a.k / G), r1 = (int)((int64_t)(w + 1) * a.k / G);
         if (tid < r1 - r0) a.iota_out[r0 + tid] = r0 + tid;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
         }
         __syncthreads();
         if (!sm.flag) {  // gave up: every partial computed here, bitwise as its workgroup stores it
-            for (int v = 0; v < G; ++v) rows_partial<KX>(a, v, sm, xs);
+            for (int v = 0; v < G; ++v) rows_partial<H>(a, v, sm, xs);
             __builtin_amdgcn_s_waitcnt(0);
         }
     }
@@ -336,8 +337,8 @@ hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, i
     a.k = k;
     a.G = G;
     a.act = act;
-    if (d == 4096) stage2_rows_kernel<4><<<G, kRT, 0, st>>>(a);
-    else stage2_rows_kernel<8><<<G, kRT, 0, st>>>(a);
+    if (d == 4096) stage2_rows_kernel<2><<<G, kRT, 0, st>>>(a);
+    else stage2_rows_kernel<1><<<G, kRT, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -351,7 +352,7 @@ int rows_groups()
     if (c) return c - 1;
     int cus = 0, g = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-        const void *fns[] = {(const void *)stage2_rows_kernel<4>, (const void *)stage2_rows_kernel<8>};
+        const void *fns[] = {(const void *)stage2_rows_kernel<2>, (const void *)stage2_rows_kernel<1>};
         int occ = 1 << 30;
         for (const void *f : fns) {
             int n = 0;
