@@ -216,7 +216,7 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     const ProxyPlan pp = proxy_plan(d, F, B, mode);
     size_t part_rows = (size_t)pp.S * B;
     if ((size_t)proxy_batch_splits((int)d) * B > part_rows) part_rows = (size_t)proxy_batch_splits((int)d) * B;
-    if (fused_supported(B, d, F)) {
+    if (fused_supported(B, d, F, mode == PROX_Q_INT4_G128 ? 4 : 8)) {
         const FusedPlan fp = fused_plan(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
         if ((size_t)fp.S > part_rows) part_rows = fp.S;
     }
@@ -295,7 +295,7 @@ prox_status run_stage1(const void *x, int64_t B, const prox_weights *w, const pr
 {
     const int64_t d = w->d_model, F = w->d_ff;
     const int dt = enum_int(w->dtype) == PROX_F32 ? 0 : 1;
-    if (fused_supported(B, d, F)) {  // one kernel; its counters are zero on entry
+    if (fused_supported(B, d, F, enum_int(p->mode) == PROX_Q_INT4_G128 ? 4 : 8)) {  // its counters are zero on entry
         TRY_HIP(mark(ev, 0, st));
         TRY_HIP(launch_stage1_fused(dt, enum_int(p->mode) == PROX_Q_INT4_G128 ? 4 : 8, x, (int)d, (int)F, (int)k_in, (int)k,
                                     (const uint8_t *)p->codes, (const float *)p->scales, ws.proxy_part, score, sel,
@@ -797,7 +797,8 @@ prox_status prox_chain_forward(void *h, int64_t batch, const prox_weights *layer
         // selection of a batch) normalizes h itself, bitwise as the RMSNorm
         // kernel, and hands RMSNorm(h) to Stage 2 in xn: no RMSNorm launch
         const Workspace ws = layout(w0.d_model, w0.d_ff, batch, enum_int(proxies[0].mode), workspace);
-        const bool fused = batch == 1 && fused_supported(1, w0.d_model, w0.d_ff);
+        const bool fused =
+            batch == 1 && fused_supported(1, w0.d_model, w0.d_ff, enum_int(proxies[0].mode) == PROX_Q_INT4_G128 ? 4 : 8);
         for (int64_t l = 0; l < n_layers; ++l) {
             const prox_proxy &p = proxies[l];
             if (fused) {

@@ -52,7 +52,8 @@ struct BatchPlan {
 
 // Single-token Stage 1 in one kernel (stage1_fused.hip).
 constexpr int kFusedMaxD = 8192;       // inputs (d_model)
-constexpr int kFusedMaxF = 16384;      // channels (d_ff): all scores fit in LDS
+constexpr int kFusedMaxF = 16384;      // channels whose top-k the kernel runs itself (scores in one workgroup)
+constexpr int kFusedGemvMaxF = 65520;  // channels it scores (larger d_ff: the top-k is a second launch)
 constexpr int kFusedScoreSlot = 511;   // counter of finished channel blocks
 
 struct FusedPlan {
@@ -62,7 +63,7 @@ struct FusedPlan {
 };
 
 FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
-bool fused_supported(int64_t B, int64_t d, int64_t F);
+bool fused_supported(int64_t B, int64_t d, int64_t F, int qbits);
 // act: the gate activation (0 silu, 1 gelu tanh form); signal: the
 // selection signal (0 |act(g~) u~|, 1 |act(g~)|, 2 |u~|).
 // norm_eps >= 0: x is the residual stream h and every workgroup uses

@@ -18,6 +18,9 @@
 // the last channel block to finish (ticket) loads all F scores and writes
 // the k selected channel indices in ascending order.  Bitwise deterministic.
 //
+// Above kFusedMaxF channels the kernel stops at the scores (k = 0 inside) and
+// launch_stage1_fused adds a top-k launch.
+//
 // Counters: counters[cb] and counters[kFusedScoreSlot] must be zero on
 // entry; the last arriver of each ticket resets it, so a completed launch
 // leaves them zero again.
@@ -37,7 +40,7 @@ constexpr int kFusedSlots = 512;  // workgroups resident at once (two per CU)
 template <int QBITS>
 struct Fused;
 template <> struct Fused<8> {  // 4 signed bytes -> channels c..c+3
-    static constexpr int CPL = 4, RMAX = 1024, GRAN = 32, NG = 1;
+    static constexpr int CPL = 4, RMAX = 2048, GRAN = 32, NG = 1;
     static __device__ __forceinline__ void decode(uint32_t w, float *q)
     {
 #pragma unroll
@@ -45,7 +48,7 @@ template <> struct Fused<8> {  // 4 signed bytes -> channels c..c+3
     }
 };
 template <> struct Fused<4> {  // 8 biased nibbles; byte p holds channels 2p (low), 2p+1 (high)
-    static constexpr int CPL = 8, RMAX = 512, GRAN = 128, NG = 512 / 128;
+    static constexpr int CPL = 8, RMAX = 1024, GRAN = 128, NG = 1024 / 128;
     static __device__ __forceinline__ void decode(uint32_t w, float *q)
     {
         const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
@@ -370,19 +373,29 @@ FusedPlan fused_plan(int qbits, int64_t d, int64_t F)
     return p;
 }
 
-bool fused_supported(int64_t B, int64_t d, int64_t F) { return B == 1 && d <= kFusedMaxD && F <= kFusedMaxF; }
+// Beyond kFusedMaxF channels only the int4 proxy takes this kernel (the scores,
+// then a top-k launch): measured at 8192 x 28672, keep 0.4, Stage 1 takes
+// 51.1 us this way against 57.0 us for the input-selection, vector-ALU proxy
+// and top-k launches; with the int8 proxy (188 MB) it took 59.5 against 57.0.
+bool fused_supported(int64_t B, int64_t d, int64_t F, int qbits)
+{
+    if (B != 1 || d > kFusedMaxD) return false;
+    return F <= kFusedMaxF || (qbits == 4 && F <= kFusedGemvMaxF);
+}
 
 hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F, int k_in, int k,
                                const uint8_t *codes, const float *scales, float *part, float *score, int32_t *sel,
                                uint32_t *counters, int act, int signal, hipStream_t st, float norm_eps, void *xn_out)
 {
-    if (!fused_supported(1, d, F)) return hipErrorInvalidValue;
+    if (!fused_supported(1, d, F, qbits)) return hipErrorInvalidValue;
     const FusedPlan pl = fused_plan(qbits, d, F);
     const int kx = (d + kFT - 1) / kFT;
-    const int kf = (F + kFT - 1) / kFT;
+    const bool topk_inside = F <= kFusedMaxF;  // else the kernel only scores, and the top-k is a second launch
+    const int kf = topk_inside ? (F + kFT - 1) / kFT : 32;
+    const int k_kernel = topk_inside ? k : 0;
     const dim3 grid(pl.n_cblocks, pl.S);
 #define L1(T, Q, KXV, KFV)                                                                               \
-    stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k, codes, scales, \
+    stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k_kernel, codes, scales, \
                                                              pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
                                                              counters, act, signal, norm_eps, (T *)xn_out)
 #define L2(T, Q)                                       \
@@ -403,7 +416,9 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
     }
 #undef L2
 #undef L1
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || topk_inside || k <= 0) return e;
+    return launch_topk(score, F, k, sel, st);
 }
 
 }  // namespace prox
