@@ -335,11 +335,11 @@ prox_status run_stage2(const void *x, int64_t B, const prox_weights *w, const in
         TRY_HIP(mark(ev, 4, st));
         return hip_status(mark(ev, 5, st));
     }
-    if (B == 1 && dt == 1 && sw.fmt == 0 && ws.ypart) {  // bf16: one workgroup per CU streams whole channels
+    if (B == 1 && dt == 1 && ws.ypart) {  // bf16 token: one workgroup per CU streams whole channels
         const int G = rows_groups();
         if (G && rows_supported(d, w->d_ff, k, G)) {
-            TRY_HIP(launch_stage2_rows(x, (int)d, (int)w->d_ff, sel, (int)k, sw.w_gu, sw.w_down_t, residual, out,
-                                       iota_out, ws.ypart, ws.counters, sw.act, o.spin_ticks, G, st));
+            TRY_HIP(launch_stage2_rows(x, (int)d, (int)w->d_ff, sel, (int)k, sw, residual, out, iota_out, ws.ypart,
+                                       ws.counters, o.spin_ticks, G, st));
             TRY_HIP(mark(ev, 4, st));
             return hip_status(mark(ev, 5, st));
         }

@@ -161,8 +161,8 @@ hipError_t launch_stage2_fused(int dtype, const S2Weights &w, const void *x, int
                                float *s_sp, float *part, const void *residual, void *out, uint32_t *counters,
                                int32_t *iota_out, hipStream_t st, uint64_t spin_ticks = 0);
 hipError_t launch_fill_out(int dtype, int B, int d, const void *residual, void *out, hipStream_t st);
-// Stage 2 for one bf16 token with bf16 weights, d_model 4096 or 8192, in one
-// launch of G workgroups, one per CU (stage2_rows.hip).  ypart: G * d floats.
+// Stage 2 for one bf16 token with bf16 or FP8 weights, d_model 4096 or 8192,
+// in one launch of G workgroups, one per CU (stage2_rows.hip).  ypart: G * d floats.
 // Counter words: the 64-bit arrival count at kRowsArriveSlot and the release
 // words at s2_sync_line(kRowsReleaseBase + i), i < G; they hold launch numbers
 // (they only grow), so they are not zero between calls; a zero fill restarts
@@ -172,9 +172,9 @@ constexpr int kRowsMaxChan = 128;      // channels per workgroup
 constexpr int kRowsArriveSlot = 3072;  // two words, 8-byte aligned
 constexpr int kRowsReleaseBase = 1024; // sync lines 1024.. (the single-token Stage 2 uses < 1024)
 bool rows_supported(int64_t d, int64_t F, int64_t k, int G);
-hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, int k, const void *w_gu,
-                              const void *w_dt, const void *residual, void *out, int32_t *iota_out, float *ypart,
-                              uint32_t *counters, int act, uint64_t spin_ticks, int G, hipStream_t st);
+hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, int k, const S2Weights &w,
+                              const void *residual, void *out, int32_t *iota_out, float *ypart, uint32_t *counters,
+                              uint64_t spin_ticks, int G, hipStream_t st);
 // Workgroups the rows kernel uses on the current device (one per CU, at most
 // kRowsMaxGroups), or 0 if a CU cannot hold one of its workgroups.
 int rows_groups();

@@ -1,17 +1,20 @@
-// Stage 2 of Prox for one bf16 token with bf16 weights ("Stage 2: Exact
-// Sparse Computation"): on the selected channels only, g = W_gate x,
-// u = W_up x, s = act(g) u and y = sum_j s_j W_down[:, j], for d_model 4096
-// or 8192.
+// Stage 2 of Prox for one bf16 token ("Stage 2: Exact Sparse Computation"):
+// on the selected channels only, g = W_gate x, u = W_up x, s = act(g) u and
+// y = sum_j s_j W_down[:, j], for d_model 4096 or 8192, with bf16 weights or
+// FP8 E4M3 weights with per-row scales (the gate and up scales multiply the
+// finished dot products, the down scale each output).
 //
 // One 1024-thread workgroup per CU.  Workgroup w takes the selected channels
 // of rank [wk/G, (w+1)k/G) and streams all three rows of each: the gate and
 // up rows give s_j, which scales the down row into a partial y of d columns
 // held in registers.  No workgroup waits for another before its partial is
 // stored, so the gate/up -> down dependency never crosses workgroups.
-//  - A row is covered by a group of d / 8 threads, thread t holding columns
-//    [8t, 8t + 8) (one 16-byte load per row): at d_model 4096 the two halves
-//    of the workgroup are two groups and take alternate channels, at 8192
-//    the whole workgroup is one group.  Each group takes 3 channels a round;
+//  - A row is covered by a group of threads, each holding the columns of one
+//    16-byte load per row (8 bf16 weights or 16 FP8 codes): with bf16 weights
+//    the two halves of the workgroup are two groups at d_model 4096 and the
+//    whole workgroup one group at 8192; with FP8 weights four and two.  The
+//    groups take channels in turn.  Each group takes 3 channels a round (2
+//    with FP8, whose 16 columns per thread need more registers);
 //    a round's rows are requested together and the next round's before the
 //    current one is reduced; g and u are added over lanes and the group's
 //    waves in a fixed order.  The groups' partials are added (first +
@@ -47,8 +50,10 @@ constexpr int kRSliceCols = 32;   // columns of a slice
 
 struct RowsArgs {
     const uint16_t *x;         // [d] bf16
-    const uint16_t *w_gu;      // [F][2][d]
-    const uint16_t *w_dt;      // [F][d]
+    const void *w_gu;          // [F][2][d] bf16, or FP8 E4M3 codes
+    const void *w_dt;          // [F][d] bf16, or FP8 E4M3 codes
+    const float *gsc;          // FP8: [F][2] gate and up row scales (else null)
+    const float *dsc;          // FP8: [d] down row scales, one per output (else null)
     const int32_t *sel;        // [k] ascending, or null: channel r at rank r
     const uint16_t *residual;  // [d] or null (may alias out)
     uint16_t *out;             // [d]
@@ -59,38 +64,63 @@ struct RowsArgs {
     int d, F, k, G, act;
 };
 
-// H: channel groups of the workgroup (2 at d_model 4096, 1 at 8192)
-template <int H>
+// A thread's piece of a row: 16 bytes, 8 consecutive bf16 columns or 16 FP8
+// E4M3 codes.
+template <typename TW> struct RowPiece;
+template <> struct RowPiece<uint16_t> {
+    using V = u32x4;
+    static constexpr int N = 8;  // columns
+    static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
+    }
+    static __device__ __forceinline__ void unpack(const V &v, float *f) { vec16<uint16_t>::unpack(v, f); }
+};
+template <> struct RowPiece<uint8_t> {
+    using V = u32x4;
+    static constexpr int N = 16;
+    static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
+    }
+    static __device__ __forceinline__ void unpack(const V &v, float *f)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e4m3x4_to_f32(v[i], f + 4 * i);
+    }
+};
+
+// H: channel groups of the workgroup, kRT / H threads each covering a row
+// (bf16: 2 at d_model 4096, 1 at 8192; FP8: 4 and 2)
+template <int H, typename TW>
 struct alignas(16) RowsSmem {
-    static constexpr int CPT = 8;   // columns per thread: a group of kRT / H threads covers a row
-    static constexpr int RC = 3;    // channels per group and round
+    static constexpr int CPT = RowPiece<TW>::N;  // columns per thread
+    static constexpr int RC = sizeof(TW) == 1 ? 2 : 3;  // channels per group and round
     union {
         struct {
             float r2[kRW][2 * RC];
             float sv[H][RC];
         } e;
-        float yhalf[kRT / 2][CPT + 1];   // H = 2: the second group's sums (padded: no bank conflicts)
+        float yg[H - 1 > 0 ? H - 1 : 1][kRT / H][CPT + 1];  // groups 1.. sums (padded: no bank conflicts)
         float sums[kRSumGroups][kRSliceCols];
     } u;
     int chan[kRowsMaxChan];
+    float gs[kRowsMaxChan][2];  // FP8: the channels' gate and up scales
     int flag;
     uint32_t epoch;
     int pos;
 };
 
-__device__ __forceinline__ u32x4 rows_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
-}
-
 // Workgroup v's partial y over its ranks, stored to ypart[v]: all threads
 // call; the value depends on v and the inputs only.
-template <int H>
-__device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H> &sm, const float (&xs)[8])
+template <int H, typename TW>
+__device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H, TW> &sm, const float (&xs)[RowPiece<TW>::N])
 {
-    constexpr int CPT = RowsSmem<H>::CPT;
-    constexpr int NV = CPT / 8;  // 16-byte vectors per row and thread
-    constexpr int RC = RowsSmem<H>::RC;
+    using RP = RowPiece<TW>;
+    using V = typename RP::V;
+    constexpr int CPT = RowsSmem<H, TW>::CPT;
+    constexpr int RC = RowsSmem<H, TW>::RC;
+    constexpr bool FP8 = sizeof(TW) == 1;
     constexpr int GT = kRT / H, GW = kRW / H;  // threads and waves of a group
     const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
     const int grp = uniform(tid / GT), ht = tid % GT;
@@ -98,51 +128,52 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H> &sm, const fl
     const int r0 = (int)((int64_t)v * a.k / a.G), r1 = (int)((int64_t)(v + 1) * a.k / a.G);
     const int nc = r1 - r0;
     __syncthreads();  // the previous user of the channel list and the LDS is done
-    if (tid < nc) sm.chan[tid] = a.sel ? min(max(a.sel[r0 + tid], 0), F - 1) : r0 + tid;  // clamped into [0, F)
+    if (tid < nc) {
+        const int j = a.sel ? min(max(a.sel[r0 + tid], 0), F - 1) : r0 + tid;  // clamped into [0, F)
+        sm.chan[tid] = j;
+        if (FP8) {
+            sm.gs[tid][0] = a.gsc[2 * j];
+            sm.gs[tid][1] = a.gsc[2 * j + 1];
+        }
+    }
     __syncthreads();
 
     float yacc[CPT];
 #pragma unroll
     for (int q = 0; q < CPT; ++q) yacc[q] = 0.0f;
-    const uint32_t rowb = 2u * (uint32_t)d;  // bytes of a row
+    const uint32_t rowb = (uint32_t)(sizeof(TW) * d);  // bytes of a row
     const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.w_gu), (short)0, (int)(2u * rowb * (uint32_t)F), CoherentBuf::kWord3);
+        const_cast<void *>(a.w_gu), (short)0, (int)(2u * rowb * (uint32_t)F), CoherentBuf::kWord3);
     const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.w_dt), (short)0, (int)(rowb * (uint32_t)F), CoherentBuf::kWord3);
+        const_cast<void *>(a.w_dt), (short)0, (int)(rowb * (uint32_t)F), CoherentBuf::kWord3);
     const uint32_t goob = 2u * rowb * (uint32_t)F, doob = rowb * (uint32_t)F;
-    const uint32_t coff = (uint32_t)(ht * CPT * 2);
-    u32x4 ag[RC][NV], au[RC][NV], ad[RC][NV], bg[RC][NV], bu[RC][NV], bd[RC][NV];
+    const uint32_t coff = (uint32_t)(ht * CPT * sizeof(TW));
+    V ag[RC], au[RC], ad[RC], bg[RC], bu[RC], bd[RC];
     // a round's rows: list entries (rd RC + c) H + grp; past the list the
     // offsets are out of range and read zero without touching memory
-    auto issue = [&](u32x4(&vg)[RC][NV], u32x4(&vu)[RC][NV], u32x4(&vd)[RC][NV], int rd) {
+    auto issue = [&](V(&vg)[RC], V(&vu)[RC], V(&vd)[RC], int rd) {
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             const int i = (rd * RC + c) * H + grp;
             const bool live = i < nc;
             const uint32_t j = (uint32_t)sm.chan[live ? i : 0];
-#pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                vg[c][q] = rows_ld16(grs, live ? j * 2u * rowb + coff + 16u * q : goob);
-                vu[c][q] = rows_ld16(grs, live ? j * 2u * rowb + rowb + coff + 16u * q : goob);
-                vd[c][q] = rows_ld16(drs, live ? j * rowb + coff + 16u * q : doob);
-            }
+            vg[c] = RP::load(grs, live ? j * 2u * rowb + coff : goob);
+            vu[c] = RP::load(grs, live ? j * 2u * rowb + rowb + coff : goob);
+            vd[c] = RP::load(drs, live ? j * rowb + coff : doob);
         }
     };
-    auto process = [&](const u32x4(&vg)[RC][NV], const u32x4(&vu)[RC][NV], const u32x4(&vd)[RC][NV], int rd) {
+    auto process = [&](const V(&vg)[RC], const V(&vu)[RC], const V(&vd)[RC], int rd) {
         float pg[RC], pu[RC];
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             float g = 0.0f, u = 0.0f;
+            float fg[CPT], fu[CPT];
+            RP::unpack(vg[c], fg);
+            RP::unpack(vu[c], fu);
 #pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                float fg[8], fu[8];
-                vec16<uint16_t>::unpack(vg[c][q], fg);
-                vec16<uint16_t>::unpack(vu[c][q], fu);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    g = fmaf(fg[e], xs[8 * q + e], g);
-                    u = fmaf(fu[e], xs[8 * q + e], u);
-                }
+            for (int e = 0; e < CPT; ++e) {
+                g = fmaf(fg[e], xs[e], g);
+                u = fmaf(fu[e], xs[e], u);
             }
             pg[c] = wave_sum(g);
             pu[c] = wave_sum(u);
@@ -169,19 +200,21 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H> &sm, const fl
                 g += tg[ww];
                 u += tu[ww];
             }
-            sm.u.e.sv[h][c] = ((rd * RC + c) * H + h < nc) ? gate_act(a.act, g) * u : 0.0f;
+            const int i = (rd * RC + c) * H + h;
+            if (FP8 && i < nc) {  // the row scales multiply the finished dot products
+                g *= sm.gs[i][0];
+                u *= sm.gs[i][1];
+            }
+            sm.u.e.sv[h][c] = i < nc ? gate_act(a.act, g) * u : 0.0f;
         }
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             const float sv = sm.u.e.sv[grp][c];
+            float fd[CPT];
+            RP::unpack(vd[c], fd);
 #pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                float fd[8];
-                vec16<uint16_t>::unpack(vd[c][q], fd);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) yacc[8 * q + e] = fmaf(sv, fd[e], yacc[8 * q + e]);
-            }
+            for (int e = 0; e < CPT; ++e) yacc[e] = fmaf(sv, fd[e], yacc[e]);
         }
     };
     const int nr = (nc + H * RC - 1) / (H * RC);
@@ -194,37 +227,43 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H> &sm, const fl
             process(bg, bu, bd, rd + 1);
         }
     }
-    // the groups' sums added (first group + second group) and stored
+    // the groups' sums added in group order and stored by group 0
     __syncthreads();
-    if (H == 2 && grp == 1) {
+    if (grp > 0) {
 #pragma unroll
-        for (int q = 0; q < CPT; ++q) sm.u.yhalf[ht][q] = yacc[q];
+        for (int q = 0; q < CPT; ++q) sm.u.yg[grp - 1][ht][q] = yacc[q];
     }
     __syncthreads();
     if (grp == 0) {  // 16-byte device-coherent stores
         const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
             a.ypart + (int64_t)v * d, (short)0, (int)(sizeof(float) * d), CoherentBuf::kWord3);
 #pragma unroll
+        for (int h = 1; h < H; ++h)
+#pragma unroll
+            for (int q = 0; q < CPT; ++q) yacc[q] += sm.u.yg[h - 1][ht][q];
+#pragma unroll
         for (int q = 0; q < CPT; q += 4) {
             u32x4 val;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                val[e] = __float_as_uint(H == 2 ? yacc[q + e] + sm.u.yhalf[ht][q + e] : yacc[q + e]);
+            for (int e = 0; e < 4; ++e) val[e] = __float_as_uint(yacc[q + e]);
             __builtin_amdgcn_raw_buffer_store_b128(val, yrs, (int)(sizeof(float) * (ht * CPT + q)), 0,
                                                    CoherentBuf::kSc1);
         }
     }
 }
 
-template <int H>
+template <int H, typename TW>
 __global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
 {
-    __shared__ RowsSmem<H> sm;
+    __shared__ RowsSmem<H, TW> sm;
     const int tid = threadIdx.x, w = blockIdx.x, G = a.G, d = a.d;
+    constexpr int CPT = RowPiece<TW>::N;
     const int ht = tid % (kRT / H);
-    float xs[8];
-    vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4 *>(a.x + 8 * ht), xs);
-    rows_partial<H>(a, w, sm, xs);
+    float xs[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; q += 8)
+        vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4 *>(a.x + CPT * ht + q), xs + q);
+    rows_partial<H, TW>(a, w, sm, xs);
     if (a.iota_out && !a.sel) {
         const int r0 = (int)((int64_t)w * a.k / G), r1 = (int)((int64_t)(w + 1) * a.k / G);
         if (tid < r1 - r0) a.iota_out[r0 + tid] = r0 + tid;
@@ -268,7 +307,7 @@ __global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
         }
         __syncthreads();
         if (!sm.flag) {  // gave up: every partial computed here, bitwise as its workgroup stores it
-            for (int v = 0; v < G; ++v) rows_partial<H>(a, v, sm, xs);
+            for (int v = 0; v < G; ++v) rows_partial<H, TW>(a, v, sm, xs);
             __builtin_amdgcn_s_waitcnt(0);
         }
     }
@@ -301,6 +340,7 @@ __global__ __launch_bounds__(kRT, 1) void stage2_rows_kernel(RowsArgs a)
             float y = t[0];
 #pragma unroll
             for (int g = 1; g < kRSumGroups; ++g) y += t[g];
+            if (a.dsc) y *= a.dsc[cA + tid];
             if (a.residual) y += __uint_as_float((uint32_t)a.residual[cA + tid] << 16);
             a.out[cA + tid] = f32_to_bf16(y);
         }
@@ -316,15 +356,18 @@ bool rows_supported(int64_t d, int64_t F, int64_t k, int G)
     return (k + G - 1) / G <= kRowsMaxChan;
 }
 
-hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, int k, const void *w_gu,
-                              const void *w_dt, const void *residual, void *out, int32_t *iota_out, float *ypart,
-                              uint32_t *counters, int act, uint64_t spin_ticks, int G, hipStream_t st)
+hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, int k, const S2Weights &w,
+                              const void *residual, void *out, int32_t *iota_out, float *ypart, uint32_t *counters,
+                              uint64_t spin_ticks, int G, hipStream_t st)
 {
     if (!rows_supported(d, F, k, G)) return hipErrorInvalidValue;
+    if (w.fmt == 1 && (!w.gu_scales || !w.down_scales)) return hipErrorInvalidValue;
     RowsArgs a;
     a.x = (const uint16_t *)x;
-    a.w_gu = (const uint16_t *)w_gu;
-    a.w_dt = (const uint16_t *)w_dt;
+    a.w_gu = w.w_gu;
+    a.w_dt = w.w_down_t;
+    a.gsc = w.fmt == 1 ? w.gu_scales : nullptr;
+    a.dsc = w.fmt == 1 ? w.down_scales : nullptr;
     a.sel = sel;
     a.residual = (const uint16_t *)residual;
     a.out = (uint16_t *)out;
@@ -336,9 +379,14 @@ hipError_t launch_stage2_rows(const void *x, int d, int F, const int32_t *sel, i
     a.F = F;
     a.k = k;
     a.G = G;
-    a.act = act;
-    if (d == 4096) stage2_rows_kernel<2><<<G, kRT, 0, st>>>(a);
-    else stage2_rows_kernel<1><<<G, kRT, 0, st>>>(a);
+    a.act = w.act;
+    if (w.fmt == 1) {
+        if (d == 4096) stage2_rows_kernel<4, uint8_t><<<G, kRT, 0, st>>>(a);
+        else stage2_rows_kernel<2, uint8_t><<<G, kRT, 0, st>>>(a);
+    } else {
+        if (d == 4096) stage2_rows_kernel<2, uint16_t><<<G, kRT, 0, st>>>(a);
+        else stage2_rows_kernel<1, uint16_t><<<G, kRT, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -352,7 +400,8 @@ int rows_groups()
     if (c) return c - 1;
     int cus = 0, g = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-        const void *fns[] = {(const void *)stage2_rows_kernel<2>, (const void *)stage2_rows_kernel<1>};
+        const void *fns[] = {(const void *)stage2_rows_kernel<2, uint16_t>, (const void *)stage2_rows_kernel<1, uint16_t>,
+                             (const void *)stage2_rows_kernel<4, uint8_t>, (const void *)stage2_rows_kernel<2, uint8_t>};
         int occ = 1 << 30;
         for (const void *f : fns) {
             int n = 0;
