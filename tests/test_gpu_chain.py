@@ -9,8 +9,10 @@ at each of the 32 layers.  The layers run in blocks of four, one test each,
 so that progress shows while the host draws 15 GB of weights.  Then the
 single chain call over all 32 layers must equal that layer-by-layer
 composition bitwise, and the end-to-end drift against an oracle-only chain
-from the same h0 is reported (not gated: a near-tie mask flip in one layer
-legitimately changes every later layer).
+from the same h0 (h and RMSNorm(h) rounded to bf16 between layers, as the
+chain keeps them) is reported (not gated: a near-tie mask flip in one layer
+legitimately changes every later layer), with the drift before each layer
+and the number of near-tie channels each teacher-forced mask differs in.
 
 Small shapes cover the other branches of the chain: fp32 layers, the int4
 proxy inside the single-token Stage 1 with the norm, d_ff above the fused
@@ -41,6 +43,13 @@ def _host(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def _bf16(a: np.ndarray) -> np.ndarray:
+    """binary64 values rounded to binary32, then to bf16 bits (round to nearest even): the
+    activation dtype the chain keeps h and RMSNorm(h) in."""
+    b = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def _init_state():
     if not _state:
         _state["layers"] = []  # device weights and proxies of every layer
@@ -48,6 +57,8 @@ def _init_state():
         _state["h"] = {B: to_dev(_state["h0"][B]) for B in W.batches}          # GPU chain, layer by layer
         _state["h_ref"] = {B: oracle.as_f64(_state["h0"][B]) for B in W.batches}  # oracle-only chain
         _state["done"] = 0
+        _state["drift_by_layer"] = {B: [] for B in W.batches}  # GPU chain vs oracle-only chain, before each layer
+        _state["mask_diffs"] = {B: [] for B in W.batches}      # near-tie channels the GPU mask differs in
     return _state
 
 
@@ -62,17 +73,22 @@ def test_chain32_teacher_forced(block):
             xn = P.rmsnorm(h, EPS)
             torch.cuda.synchronize()
             h_host, xn_host = _host(h), _host(xn)
+            hg, hr = oracle.as_f64(h_host), st["h_ref"][B]
+            st["drift_by_layer"][B].append(max(float(np.abs(hg[b] - hr[b]).max() / np.abs(hr[b]).max())
+                                               for b in range(B)))
             # RMSNorm in fp32 rounded to bf16: within one bf16 rounding of the oracle's
             rr = oracle.rmsnorm(h_host, EPS)
             assert np.abs(oracle.as_f64(xn_host) - rr).max() <= 2.0 ** -8 * np.abs(rr).max()
             r = run_and_check(L, xn_host, W.mode, W.input_keep, W.sparsities[0], residual=h_host,
                               label="chain32 B=%d layer %d" % (B, l))
             st["h"][B] = r["out"]
+            st["mask_diffs"][B].append(int(len(set(r["sel"].tolist()) ^ set(r["ref"]["sel"].tolist())) // 2))
             # the oracle-only chain: its own norm, mask and output on its own h
+            # (h and RMSNorm(h) kept in bf16 between layers, as the GPU chain keeps them)
             hr = st["h_ref"][B]
-            ref = oracle.prox_forward(oracle.rmsnorm(hr, EPS), L.wg, L.wu, L.wd, L.oracle_proxy(W.mode),
+            ref = oracle.prox_forward(_bf16(oracle.rmsnorm(hr, EPS)), L.wg, L.wu, L.wd, L.oracle_proxy(W.mode),
                                       W.input_keep, W.sparsities[0], W.mode)
-            st["h_ref"][B] = hr + ref["y"]
+            st["h_ref"][B] = oracle.as_f64(_bf16(hr + ref["y"]))
         L.drop_host()
         st["layers"].append((L.w, L.proxy(W.mode)))
         st["done"] = l + 1
@@ -94,8 +110,16 @@ def test_chain32_single_call_bitwise_and_drift():
         assert torch.equal(h_chain.view(torch.int16), st["h"][B].view(torch.int16)), "B=%d" % B
         y_gpu, y_ref = from_dev(h_chain), st["h_ref"][B]
         per_tok = [float(np.abs(y_gpu[b] - y_ref[b]).max() / np.abs(y_ref[b]).max()) for b in range(B)]
+        dl = st["drift_by_layer"][B]
+        first = next((l for l, v in enumerate(dl) if v > 1e-2), None)
         drift[str(B)] = {"max_rel_err_per_token": max(per_tok), "mean_rel_err_per_token": float(np.mean(per_tok)),
-                         "h_maxabs": float(np.abs(y_ref).max())}
+                         "h_maxabs": float(np.abs(y_ref).max()),
+                         "drift_before_layer": [float("%.3g" % v) for v in dl],
+                         "first_layer_input_beyond_1e-2": first,
+                         "mask_channels_differing_from_oracle_per_layer": st["mask_diffs"][B]}
+        log("chain32 B=%d drift before each layer: %s" % (B, " ".join("%.2g" % v for v in dl)))
+        log("chain32 B=%d channels differing from the oracle's mask, per layer (teacher-forced, near-ties): %s"
+            % (B, st["mask_diffs"][B]))
         log("chain32 B=%d end-to-end drift vs the oracle-only chain: max %.3g, mean %.3g"
             % (B, max(per_tok), float(np.mean(per_tok))))
     if os.path.isdir("gpurun_out"):
