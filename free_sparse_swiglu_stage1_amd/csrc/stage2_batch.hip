@@ -44,9 +44,7 @@ constexpr int kBT = 16;                      // token slots of a tile (B padded)
 constexpr int kGuWaves = 4;                  // waves per gate/up workgroup
 constexpr int kGuWaveK = 256;                // inputs per wave
 constexpr int kGuK = kGuWaves * kGuWaveK;    // inputs per gate/up workgroup
-constexpr int kXPitch = kGuK + 8;            // LDS x row, bf16 elements (16-byte pad: no bank conflicts)
 constexpr int kDnWaves = 8;                  // waves per down workgroup
-constexpr int kDnCols = 128;                 // output columns per down workgroup
 constexpr int kGuSplitK = 512;               // inputs per chunk of a split gate/up tile
 constexpr int kDnTargetWgs = 256;           // down workgroups aimed at (column tiles x rank splits)
 constexpr int kDnMaxKps = 64;                // K-steps (32 ranks) per down workgroup, at most
