@@ -8,7 +8,8 @@ smaller layer with a residual, then a batch of four, then the first layer
 again (the array keeps the previous call's contents; the counters must be
 back at zero for each next call).  The outputs also meet the oracle's
 acceptance rules.  No device memory is taken by the calls once the array is
-loaded.  A layer too large for the array is refused on the host."""
+loaded.  A layer too large for the array is refused on the host.  Forwards
+captured in a HIP graph and replayed give the eager output bitwise."""
 import numpy as np
 import pytest
 import torch
@@ -73,3 +74,33 @@ def test_noalloc_refuses_layers_beyond_the_array():
     with pytest.raises(P.ProxError) as e:
         P.ffn_forward_noalloc(x, w, p, 0.5, 0.7, torch.empty_like(x))
     assert e.value.status == P.ERR_SCRATCH_LIMIT
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point serves capture it: after a first call has
+    set the array up, forwards captured in a HIP graph and replayed (with eager
+    calls between the replays) give the eager output bitwise."""
+    L = Layer(4096, 14336, 0.02, "bf16", seed=5)
+    x = to_dev(synth.make_x(1, 4096, "bf16", seed=6))
+    p = L.proxy("int8_row")
+    ref = torch.empty_like(x)
+    P.ffn_forward_noalloc(x, L.w, p, 0.5, 0.7, ref)
+    torch.cuda.synchronize()
+    out = torch.empty_like(x)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(3):
+                P.ffn_forward_noalloc(x, L.w, p, 0.5, 0.7, out)
+    torch.cuda.synchronize()
+    eager = torch.empty_like(x)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        P.ffn_forward_noalloc(x, L.w, p, 0.5, 0.7, eager)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))
