@@ -216,9 +216,10 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     const ProxyPlan pp = proxy_plan(d, F, B, mode);
     size_t part_rows = (size_t)pp.S * B;
     if ((size_t)proxy_batch_splits((int)d) * B > part_rows) part_rows = (size_t)proxy_batch_splits((int)d) * B;
+    size_t part_floats = part_rows * 2 * F;
     if (fused_supported(B, d, F, mode == PROX_Q_INT4_G128 ? 4 : 8)) {
-        const FusedPlan fp = fused_plan(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
-        if ((size_t)fp.S > part_rows) part_rows = fp.S;
+        const size_t f = (size_t)fused_part_floats(mode == PROX_Q_INT4_G128 ? 4 : 8, d, F);
+        if (f > part_floats) part_floats = f;
     }
     const int down_s_max = 2 * ceil_div(F, kDownRowsPerWave * kDownWaves);  // 4-token passes: half-size workgroups
     size_t off = 0;
@@ -227,7 +228,7 @@ Workspace layout(int64_t d, int64_t F, int64_t B, int mode, void *base)
     auto take = [&](size_t n) { char *p = b ? b + off : nullptr; off += align256(n); return p; };
     w.counters = (uint32_t *)take(sizeof(uint32_t) * kZeroWords);
     w.xh = (float *)take(sizeof(float) * B * d);
-    w.proxy_part = (float *)take(sizeof(float) * part_rows * 2 * F);
+    w.proxy_part = (float *)take(sizeof(float) * part_floats);
     w.score = (float *)take(sizeof(float) * F);
     w.sel = (int32_t *)take(sizeof(int32_t) * F);
     w.s_sp = (float *)take(sizeof(float) * B * F);

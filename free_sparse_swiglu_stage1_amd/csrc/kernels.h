@@ -63,6 +63,10 @@ struct FusedPlan {
 };
 
 FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
+// Floats of `part` the kernel uses: the split partials (S x 2 x F), then,
+// when the top-k runs inside (F <= kFusedMaxF), 256 16-bit score counts per
+// channel block.
+int64_t fused_part_floats(int qbits, int64_t d, int64_t F);
 bool fused_supported(int64_t B, int64_t d, int64_t F, int qbits);
 // act: the gate activation (0 silu, 1 gelu tanh form); signal: the
 // selection signal (0 |act(g~) u~|, 1 |act(g~)|, 2 |u~|).

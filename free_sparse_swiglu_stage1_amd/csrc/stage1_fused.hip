@@ -14,9 +14,11 @@
 //  3. adds its eight waves' sums in LDS in a fixed order and publishes the
 //     split's partial g~ / u~ with coherent 64-bit stores.
 // The last split of a channel block to finish (ticket) adds the partials in
-// split order and publishes score_j = |silu(g~_j) u~_j| for its channels;
-// the last channel block to finish (ticket) loads all F scores and writes
-// the k selected channel indices in ascending order.  Bitwise deterministic.
+// split order and publishes score_j = |silu(g~_j) u~_j| for its channels,
+// with a count of them by exponent byte (256 bins); the last channel block to
+// finish (ticket) loads all F scores and those counts, whose sum is the first
+// radix pass of the top-k, and writes the k selected channel indices in
+// ascending order.  Bitwise deterministic.
 //
 // Above kFusedMaxF channels the kernel stops at the scores (k = 0 inside) and
 // launch_stage1_fused adds a top-k launch.
@@ -36,6 +38,7 @@ constexpr int kFT = 512;          // threads per workgroup
 constexpr int kFW = kFT / 64;     // waves per workgroup
 constexpr int kFRows = 32;        // kept inputs in flight per wave
 constexpr int kFusedSlots = 512;  // workgroups resident at once (two per CU)
+constexpr int kCoarseBins = 256;  // score counts per channel block: bits 30..23 of the key
 
 template <int QBITS>
 struct Fused;
@@ -93,6 +96,8 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     const int cb = blockIdx.x, s = blockIdx.y;
     const int i0 = s * R, i1 = min(d, i0 + R);
     const int64_t half_bytes = (int64_t)F * QBITS / 8;
+    // the channel blocks' score counts follow the split partials
+    uint32_t *const blk_hist = reinterpret_cast<uint32_t *>(part + (int64_t)S * 2 * F);
     const int c = cb * CB + lane * CPL;
     const int cc = c < F ? c : 0;
 
@@ -278,6 +283,9 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
         sm.p.red[wv][1][lane * CPL + n] = acc[1][n];
     }
     __syncthreads();
+    // the list is read no more: its first words become the score counts
+    uint32_t *const chist = reinterpret_cast<uint32_t *>(sm.li);
+    if (k > 0 && tid < kCoarseBins) chist[tid] = 0u;
     for (int e = tid; e < CB; e += kFT) {  // e = (half, channel pair)
         const int h = e / (CB / 2), jj = 2 * (e % (CB / 2)), j = cb * CB + jj;
         if (j < F) {
@@ -329,21 +337,68 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
                 sc[q] = salience(signal, act, g, u);
             }
             store_agent2(&score[j], sc[0], sc[1]);
+            if (k > 0) {  // F is even: both channels exist
+                atomicAdd(&chist[(__float_as_uint(sc[0]) & 0x7FFFFFFFu) >> 23], 1u);
+                atomicAdd(&chist[(__float_as_uint(sc[1]) & 0x7FFFFFFFu) >> 23], 1u);
+            }
+        }
+    }
+    if (k > 0) {  // the counts as 16-bit fields (a block has < 2^16 channels), four bins a store
+        __syncthreads();
+        if (tid < kCoarseBins / 4) {
+            const u32x4 c4 = *reinterpret_cast<const u32x4 *>(&chist[4 * tid]);
+            store_agent2(reinterpret_cast<float *>(&blk_hist[(cb * kCoarseBins + 4 * tid) / 2]),
+                         __uint_as_float(c4[0] | (c4[1] << 16)), __uint_as_float(c4[2] | (c4[3] << 16)));
         }
     }
     if (!publish_and_ticket(&counters[kFusedScoreSlot], (uint32_t)n_cblocks, &sm.flag)) return;
 
     // ---- 4. the last channel block: top-k over all F scores, every
-    // coherent load issued before any is used
+    // coherent load issued before any is used: the counts first
     if (k <= 0) return;
+    // the blocks' counts: thread t loads bins 4m..4m+3 (m = t mod 64) of the
+    // blocks t / 64 + 8i, as two words of two 16-bit fields (blocks past
+    // n_cblocks read 0)
+    constexpr int HB = kFusedMaxF / CB / 8;
+    static_assert(kFT == 8 * (kCoarseBins / 4), "eight threads per four bins");
+    const CoherentBuf hbuf(blk_hist, (uint32_t)(sizeof(uint16_t) * kCoarseBins * n_cblocks));
+    float hc[HB][2];
+#pragma unroll
+    for (int i = 0; i < HB; ++i)
+        hbuf.load2(8u * (uint32_t)((8 * i + (tid >> 6)) * (kCoarseBins / 4) + (tid & 63)), hc[i][0], hc[i][1]);
+    // then the scores: the counts' crossing is found while they arrive (loads retire in order)
     uint32_t fk[KF];
 #pragma unroll
     for (int r = 0; r < KF; ++r) fk[r] = __float_as_uint(load_agent(&score[min(slot_index<KF>(r), F - 1)]));
+    uint32_t w0 = 0, w1 = 0;  // fields add without carry: at most HB x CB = 2048 per field
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+        w0 += __float_as_uint(hc[i][0]);
+        w1 += __float_as_uint(hc[i][1]);
+    }
+    *reinterpret_cast<u32x4 *>(&sm.sel.hist[(tid >> 6) * kCoarseBins + 4 * (tid & 63)]) =
+        u32x4{w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+    __syncthreads();
+    // first radix pass (bits 30..23, scores being sign-free) from the counts,
+    // then the passes over bits 22..0 below the crossing bin
+    uint32_t h1[1] = {0u};
+    if (tid < kCoarseBins) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) h1[0] += sm.sel.hist[g * kCoarseBins + tid];
+    }
+    find_crossing<kFT, 1>(h1, (uint32_t)k, sm.sel.scratch, sm.sel.found);
+    const uint32_t prefix = uniform_u32(sm.sel.found[0]) << 23;
+    const uint32_t rem = (uint32_t)k - uniform_u32(sm.sel.found[1]), in_bin = uniform_u32(sm.sel.found[2]);
     // slots past F get the key 0xFFFFFFFF, which no selection step takes
 #pragma unroll
     for (int r = 0; r < KF; ++r) fk[r] = (slot_index<KF>(r) < F) ? (fk[r] & 0x7FFFFFFFu) : 0xFFFFFFFFu;
-    // scores are sign-free: the window is bits 30..0
-    const SelectResult st = block_select_window<kFT, KF>(fk, F, k, 30, 0, sm.sel);
+    SelectResult st;
+    if (rem == in_bin) {  // the whole bin is selected
+        st.T = prefix;
+        st.need_eq = st.count_eq = rem;
+    } else {
+        st = radix_select_from<kFT, KF>(fk, F, prefix, 0xFF800000u, rem, 22, 0, sm.sel);
+    }
     auto put = [&](int i, uint32_t pos) {
         if (pos < (uint32_t)k) sel[pos] = i;
     };
@@ -373,6 +428,12 @@ FusedPlan fused_plan(int qbits, int64_t d, int64_t F)
     return p;
 }
 
+int64_t fused_part_floats(int qbits, int64_t d, int64_t F)
+{
+    const FusedPlan p = fused_plan(qbits, d, F);
+    return (int64_t)p.S * 2 * F + (F <= kFusedMaxF ? (int64_t)kCoarseBins / 2 * p.n_cblocks : 0);
+}
+
 // Beyond kFusedMaxF channels only the int4 proxy takes this kernel (the scores,
 // then a top-k launch): measured at 8192 x 28672, keep 0.4, Stage 1 takes
 // 51.1 us this way against 57.0 us for the input-selection, vector-ALU proxy
@@ -398,14 +459,17 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
     stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k_kernel, codes, scales, \
                                                              pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
                                                              counters, act, signal, norm_eps, (T *)xn_out)
-#define L2(T, Q)                                       \
-    do {                                               \
-        if (kx <= 2 && kf <= 16) L1(T, Q, 2, 16);      \
-        else if (kx <= 2) L1(T, Q, 2, 32);             \
-        else if (kx <= 8 && kf <= 16) L1(T, Q, 8, 16); \
-        else if (kx <= 8) L1(T, Q, 8, 32);             \
-        else if (kf <= 16) L1(T, Q, 16, 16);           \
-        else L1(T, Q, 16, 32);                         \
+#define L3(T, Q, KXV)                               \
+    do {                                            \
+        if (kf <= 16) L1(T, Q, KXV, 16);            \
+        else if (kf <= 28) L1(T, Q, KXV, 28);       \
+        else L1(T, Q, KXV, 32);                     \
+    } while (0)
+#define L2(T, Q)                 \
+    do {                         \
+        if (kx <= 2) L3(T, Q, 2);      \
+        else if (kx <= 8) L3(T, Q, 8); \
+        else L3(T, Q, 16);             \
     } while (0)
     if (dtype == 0) {
         if (qbits == 8) L2(float, 8);
@@ -415,6 +479,7 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
         else L2(uint16_t, 4);
     }
 #undef L2
+#undef L3
 #undef L1
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || topk_inside || k <= 0) return e;
