@@ -315,6 +315,35 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
     return base + incl - v;
 }
 
+// block_excl_scan, and in the same barrier round the block sum of one
+// wave-uniform value per wave (through *wave_sum_out).  scratch: >= 2 NW.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_and_sum(uint32_t v, uint32_t wave_val, uint32_t *scratch,
+                                                            uint32_t *total, uint32_t *wave_sum_out)
+{
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == kWave - 1) scratch[wid] = incl;
+    if (lane == 0) scratch[NW + wid] = wave_val;
+    __syncthreads();
+    uint32_t sw[NW], sv[NW];
+    lds_words<NW>(scratch, sw);
+    lds_words<NW>(scratch + NW, sv);
+    uint32_t base = 0, tot = 0, vs = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        base += (w < wid) ? sw[w] : 0u;
+        tot += sw[w];
+        vs += sv[w];
+    }
+    __syncthreads();
+    *total = tot;
+    *wave_sum_out = vs;
+    return base + incl - v;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_and_or(uint32_t a, uint32_t o, uint32_t *scratch, uint32_t *or_out)
 {

@@ -47,8 +47,10 @@ struct SelectResult {
 template <int MAXN>
 struct alignas(16) SelectSmem {
     static constexpr int W = MAXN / 32;  // bitmap words
-    static_assert(MAXN % 64 == 0 && W <= kPassBins, "bitmap sizes");
-    uint32_t hist[kPassBins * kHistCopiesMax];  // radix counters; afterwards the bitmap of keys equal to T
+    static_assert(MAXN % 64 == 0 && W <= kPassBins * (kHistCopiesMax - 1), "bitmap sizes");
+    // radix counters; afterwards, from word kPassBins, the bitmap of keys
+    // equal to T (above the bins a narrow last pass reads)
+    uint32_t hist[kPassBins * kHistCopiesMax];
     uint32_t bits[W];          // selection bitmap: bit i of word i/32 = index i selected
     alignas(16) uint32_t scratch[64];
     uint32_t found[4];
@@ -155,18 +157,42 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n
         if (slot_index<KPT>(r) < n && (key[r] & known) == prefix)
             atomicAdd(&sm.hist[((key[r] >> shift) & dmask) * kHistCopies + copy], 1u);
     __syncthreads();
-    uint32_t h[BPT];
+    uint32_t bin, above, in_bin;
+    if (width <= 6) {  // uniform
+        // a narrow pass (always the last): every wave finds the crossing
+        // itself, without a barrier.  Lane l takes bin nb - 1 - l, so the
+        // inclusive scan over lanes counts the keys in that bin and above;
+        // the first lane where that reaches `remaining` holds the crossing.
+        const int lane = tid & 63, b = (1 << width) - 1 - lane;
+        uint32_t hv = 0u;
+        if (b >= 0) {
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        h[i] = 0u;
+            for (int c = 0; c < kHistCopies; ++c) hv += sm.hist[b * kHistCopies + c];
+        }
+        const uint32_t incl = wave_incl_scan(hv);
+        const uint64_t m = __ballot(b >= 0 && incl >= remaining);
+        const int L = uniform(m ? (int)__builtin_ctzll(m) : 0);  // m != 0 when remaining <= total
+        const uint32_t hl = (uint32_t)__builtin_amdgcn_readlane((int)hv, L);
+        bin = (uint32_t)((1 << width) - 1 - L);
+        above = (uint32_t)__builtin_amdgcn_readlane((int)incl, L) - hl;
+        in_bin = hl;
+    } else {
+        uint32_t h[BPT];
 #pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) h[i] += mine[i * kHistCopies + c];
+        for (int i = 0; i < BPT; ++i) {
+            h[i] = 0u;
+#pragma unroll
+            for (int c = 0; c < kHistCopies; ++c) h[i] += mine[i * kHistCopies + c];
+        }
+        find_crossing<NT, BPT>(h, remaining, sm.scratch, sm.found);
+        bin = uniform_u32(sm.found[0]);
+        above = uniform_u32(sm.found[1]);
+        in_bin = uniform_u32(sm.found[2]);
     }
-    find_crossing<NT, BPT>(h, remaining, sm.scratch, sm.found);
-    remaining -= uniform_u32(sm.found[1]);
-    prefix |= uniform_u32(sm.found[0]) << shift;
+    remaining -= above;
+    prefix |= bin << shift;
     known |= dmask << shift;
-    return uniform_u32(sm.found[2]);
+    return in_bin;
 }
 
 // Radix passes over the bits [lowest, cursor] below a known prefix, until
@@ -270,7 +296,7 @@ __device__ void selection_bitmap(const uint32_t (&key)[KPT], int n, SelectResult
             const uint64_t eq = __ballot((slot_index<KPT>(r) < n) & (key[r] == T));
             mine = (lane == r) ? eq : mine;
         }
-        if (lane < KPT) *reinterpret_cast<uint64_t *>(&sm.hist[(row0 >> 5) + 2 * lane]) = mine;
+        if (lane < KPT) *reinterpret_cast<uint64_t *>(&sm.hist[kPassBins + (row0 >> 5) + 2 * lane]) = mine;
     }
     __syncthreads();
     if (!all) {  // of the keys equal to T, the need_eq first in index order
@@ -280,7 +306,7 @@ __device__ void selection_bitmap(const uint32_t (&key)[KPT], int n, SelectResult
         uint32_t m[WPT], cnt = 0;
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
-            m[j] = (w0 + j < nw) ? sm.hist[w0 + j] : 0u;
+            m[j] = (w0 + j < nw) ? sm.hist[kPassBins + w0 + j] : 0u;
             cnt += (uint32_t)__popc(m[j]);
         }
         uint32_t tot;

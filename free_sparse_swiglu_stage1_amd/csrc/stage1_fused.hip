@@ -174,18 +174,15 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     const uint32_t T_x = uniform_u32(sr.T), need_eq = uniform_u32(sr.need_eq);
     const bool all_eq = need_eq == uniform_u32(sr.count_eq);
     // keys equal to T_x: the need_eq of lowest index are kept; avail of them
-    // are left for this split once those before it are counted
-    uint32_t avail = need_eq;
+    // are left for this split once those before it (c_eq, this wave's count)
+    // are added up, in the same barrier round as the list's first scan
+    uint32_t c_eq = 0;
     if (!all_eq) {
-        uint32_t c = 0;
 #pragma unroll
         for (int r = 0; r < KX; ++r)
-            c += (uint32_t)__popcll(__ballot((slot_index<KX>(r) < i0) & (key[r] == T_x)));
-        uint32_t before_tot;
-        (void)waves_excl_scan<kFT>(c, sm.sel.scratch, &before_tot);
-        before_tot = uniform_u32(before_tot);
-        avail = need_eq > before_tot ? need_eq - before_tot : 0u;
+            c_eq += (uint32_t)__popcll(__ballot((slot_index<KX>(r) < i0) & (key[r] == T_x)));
     }
+    uint32_t avail = need_eq;
     // the split's kept inputs, listed in ascending order: one scan of packed
     // (greater, equal) counts gives every position
     uint32_t n_gt = 0, n_eq = 0;
@@ -198,8 +195,15 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
         const bool gt = in && (all_eq ? kk >= T_x : kk > T_x);
         const bool eq = in && !all_eq && kk == T_x;
         const uint32_t v = (gt ? 1u : 0u) | (eq ? 0x10000u : 0u);
-        uint32_t tot;
-        const uint32_t before = block_excl_scan<kFT>(v, sm.sel.scratch, &tot);
+        uint32_t tot, before;
+        if (q == 0) {
+            uint32_t eq_before_split;
+            before = block_excl_scan_and_sum<kFT>(v, c_eq, sm.sel.scratch, &tot, &eq_before_split);
+            eq_before_split = uniform_u32(eq_before_split);
+            avail = need_eq > eq_before_split ? need_eq - eq_before_split : 0u;
+        } else {
+            before = block_excl_scan<kFT>(v, sm.sel.scratch, &tot);
+        }
         const uint32_t gt_before = n_gt + (before & 0xFFFFu), eq_before = n_eq + (before >> 16);
         if (gt || (eq && eq_before < avail)) {
             const uint32_t pos = gt_before + min(eq_before, avail);
