@@ -63,9 +63,9 @@ struct FusedPlan {
 };
 
 FusedPlan fused_plan(int qbits, int64_t d, int64_t F);
-// Floats of `part` the kernel uses: the split partials (S x 2 x F), then,
-// when the top-k runs inside (F <= kFusedMaxF), 256 16-bit score counts per
-// channel block.
+// Floats of `part` the kernel uses: the split partials (S x 2 x F), then 256
+// 16-bit score counts per channel block (the first radix pass of the top-k,
+// inside the kernel up to kFusedMaxF channels, else in a second launch).
 int64_t fused_part_floats(int qbits, int64_t d, int64_t F);
 bool fused_supported(int64_t B, int64_t d, int64_t F, int qbits);
 // act: the gate activation (0 silu, 1 gelu tanh form); signal: the
@@ -89,6 +89,10 @@ hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int 
 hipError_t launch_score_from_s(const float *s, int B, int F, float *score, hipStream_t st);
 hipError_t launch_gather_s(const float *s, int B, int F, const int32_t *sel, int k, float *s_sel, hipStream_t st);
 hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st);
+// The top-k after stage1_fused_kernel's scores, from its channel blocks' score
+// counts (blk_cnt: n_blocks x 128 words of 16-bit fields, n_blocks <= 128).
+hipError_t launch_topk_counts(const float *score, int n, int k, int32_t *sel, const uint32_t *blk_cnt,
+                              int n_blocks, hipStream_t st);
 
 // Stage-2 weights as the kernels read them.  fmt 0: w_gu [F][2][d] and
 // w_down_t [F][d] in the activation dtype.  fmt 1: the same layouts in FP8

@@ -360,6 +360,68 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ sc
     });
 }
 
+// The same top-k for the scores of stage1_fused_kernel beyond the channels
+// whose top-k it runs itself: its channel blocks' counts of their scores by
+// exponent byte (256 16-bit fields per block, 128 words) are summed first,
+// which is the first radix pass (bits 30..23) without a histogram of the
+// keys; the passes over bits 22..0 then count only the keys of the crossing
+// bin.  Thread t sums bins 4m..4m+3 (m = t mod 64) of the blocks t/64 + 16 i.
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_counts_kernel(const float *__restrict__ score, int n, int k,
+                                                           int32_t *__restrict__ sel,
+                                                           const uint32_t *__restrict__ blk_cnt, int n_blocks)
+{
+    constexpr int HB = 8;  // blocks a thread sums: at most 128
+    __shared__ SelectSmem<65536> sm;
+    const int tid = threadIdx.x;
+    const CoherentBuf hbuf(blk_cnt, (uint32_t)(4 * 128 * n_blocks));  // blocks past n_blocks read 0
+    float hc[HB][2];
+#pragma unroll
+    for (int i = 0; i < HB; ++i)
+        hbuf.load2(8u * (uint32_t)((16 * i + (tid >> 6)) * 64 + (tid & 63)), hc[i][0], hc[i][1]);
+    uint32_t key[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const int i = slot_index<KPT>(r);
+        key[r] = __float_as_uint(score[i < n ? i : n - 1]);
+    }
+    uint32_t w0 = 0, w1 = 0;  // 16-bit fields add without carry: at most HB x 512 each
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+        w0 += __float_as_uint(hc[i][0]);
+        w1 += __float_as_uint(hc[i][1]);
+    }
+    *reinterpret_cast<u32x4 *>(&sm.hist[(tid >> 6) * 256 + 4 * (tid & 63)]) =
+        u32x4{w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+    __syncthreads();
+    uint32_t h1[1] = {0u};
+    if (tid < 256) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) h1[0] += sm.hist[g * 256 + tid];
+    }
+    find_crossing<1024, 1>(h1, (uint32_t)k, sm.scratch, sm.found);
+    const uint32_t prefix = uniform_u32(sm.found[0]) << 23;
+    const uint32_t rem = (uint32_t)k - uniform_u32(sm.found[1]), in_bin = uniform_u32(sm.found[2]);
+    // slots past n get the key 0xFFFFFFFF, which no selection step takes
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) key[r] = (slot_index<KPT>(r) < n) ? (key[r] & 0x7FFFFFFFu) : 0xFFFFFFFFu;
+    SelectResult sr;
+    if (rem == in_bin) {  // the whole bin is selected
+        sr.T = prefix;
+        sr.need_eq = sr.count_eq = rem;
+    } else {
+        sr = radix_select_from<1024, KPT>(key, n, prefix, 0xFF800000u, rem, 22, 0, sm);
+    }
+    if (uniform_u32(sr.need_eq) == uniform_u32(sr.count_eq)) {  // no tie to break: key >= T
+        emit_at_least<1024, KPT>(key, uniform_u32(sr.T), sel, (uint32_t)k, sm);
+        return;
+    }
+    selection_bitmap<1024, KPT>(key, n, sr, sm);
+    emit_bitmap<1024>(n, sm, [&](int i, uint32_t pos) {
+        if (pos < (uint32_t)k) sel[pos] = i;
+    });
+}
+
 // ------------------------------------------------------------------------
 // host-side launchers
 // ------------------------------------------------------------------------
@@ -405,6 +467,18 @@ hipError_t launch_proxy(const ProxyPlan &pl, const float *xh, int B, int d, int 
     }
 #undef PX
     return hipGetLastError();
+}
+
+hipError_t launch_topk_counts(const float *score, int n, int k, int32_t *sel, const uint32_t *blk_cnt,
+                              int n_blocks, hipStream_t st)
+{
+    if (n_blocks < 1 || n_blocks > 128 || k < 1 || k > n) return hipErrorInvalidValue;
+    const int kpt = (n + 1023) / 1024;
+#define TK(K) \
+    if (kpt <= K) { topk_counts_kernel<K><<<1, 1024, 0, st>>>(score, n, k, sel, blk_cnt, n_blocks); return hipGetLastError(); }
+    TK(32) TK(64)
+#undef TK
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_topk(const float *score, int n, int k, int32_t *sel, hipStream_t st)

@@ -20,8 +20,9 @@
 // radix pass of the top-k, and writes the k selected channel indices in
 // ascending order.  Bitwise deterministic.
 //
-// Above kFusedMaxF channels the kernel stops at the scores (k = 0 inside) and
-// launch_stage1_fused adds a top-k launch.
+// Above kFusedMaxF channels the kernel stops at the scores and their counts
+// (topk_here = 0) and launch_stage1_fused adds a top-k launch that starts
+// from the counts.
 //
 // Counters: counters[cb] and counters[kFusedScoreSlot] must be zero on
 // entry; the last arriver of each ticket resets it, so a completed launch
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
                                                            int n_cblocks, float *__restrict__ part,
                                                            float *__restrict__ score, int32_t *__restrict__ sel,
                                                            uint32_t *__restrict__ counters, int act, int signal,
-                                                           float norm_eps, T *__restrict__ xn_out)
+                                                           float norm_eps, T *__restrict__ xn_out, int topk_here)
 {
     using Q = Fused<QBITS>;
     constexpr int CPL = Q::CPL;
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
 
     // ---- 4. the last channel block: top-k over all F scores, every
     // coherent load issued before any is used: the counts first
-    if (k <= 0) return;
+    if (k <= 0 || !topk_here) return;
     // the blocks' counts: thread t loads bins 4m..4m+3 (m = t mod 64) of the
     // blocks t / 64 + 8i, as two words of two 16-bit fields (blocks past
     // n_cblocks read 0)
@@ -435,7 +436,7 @@ FusedPlan fused_plan(int qbits, int64_t d, int64_t F)
 int64_t fused_part_floats(int qbits, int64_t d, int64_t F)
 {
     const FusedPlan p = fused_plan(qbits, d, F);
-    return (int64_t)p.S * 2 * F + (F <= kFusedMaxF ? (int64_t)kCoarseBins / 2 * p.n_cblocks : 0);
+    return (int64_t)p.S * 2 * F + (int64_t)kCoarseBins / 2 * p.n_cblocks;
 }
 
 // Beyond kFusedMaxF channels only the int4 proxy takes this kernel (the scores,
@@ -457,12 +458,13 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
     const int kx = (d + kFT - 1) / kFT;
     const bool topk_inside = F <= kFusedMaxF;  // else the kernel only scores, and the top-k is a second launch
     const int kf = topk_inside ? (F + kFT - 1) / kFT : 32;
-    const int k_kernel = topk_inside ? k : 0;
+    const int k_kernel = k;
     const dim3 grid(pl.n_cblocks, pl.S);
 #define L1(T, Q, KXV, KFV)                                                                               \
     stage1_fused_kernel<T, Q, KXV, KFV><<<grid, kFT, 0, st>>>((const T *)x, d, F, k_in, k_kernel, codes, scales, \
                                                              pl.R, pl.S, pl.n_cblocks, part, score, sel,  \
-                                                             counters, act, signal, norm_eps, (T *)xn_out)
+                                                             counters, act, signal, norm_eps, (T *)xn_out, \
+                                                             topk_inside ? 1 : 0)
 #define L3(T, Q, KXV)                               \
     do {                                            \
         if (kf <= 16) L1(T, Q, KXV, 16);            \
@@ -487,7 +489,8 @@ hipError_t launch_stage1_fused(int dtype, int qbits, const void *x, int d, int F
 #undef L1
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || topk_inside || k <= 0) return e;
-    return launch_topk(score, F, k, sel, st);
+    return launch_topk_counts(score, F, k, sel, reinterpret_cast<const uint32_t *>(part + (int64_t)pl.S * 2 * F),
+                              pl.n_cblocks, st);
 }
 
 }  // namespace prox
