@@ -116,6 +116,11 @@ def _tied_x(B, d, dtype, seed):
     # of a length that is not a multiple of 1024 (d = 2504: three splits of 864)
     (1024, 2064, "bf16", 6, "int8_row", "dup"), (768, 1040, "bf16", 8, "int8_row", "zeros"),
     (2504, 1040, "bf16", 8, "int8_row", None), (768, 1040, "bf16", 5, "int8_row", "xties"),
+    # int4 beyond 16384 channels: the fused kernel scores, then the top-k launch
+    # that starts from the channel blocks' score counts (random, duplicated and
+    # mostly-zero scores: ties across blocks and a threshold at zero)
+    (1024, 16416, "bf16", 1, "int4_g128", None), (1024, 16416, "bf16", 1, "int4_g128", "dup"),
+    (1024, 16416, "bf16", 1, "int4_g128", "zeros"),
 ])
 def test_stage1_scores_and_mask(d, F, dtype, B, mode, pattern):
     L = Layer(d, F, 0.02, dtype, seed=11, pattern=pattern if pattern != "xties" else None)
