@@ -4,7 +4,8 @@ workspace, for callers that cannot allocate device memory.
 Checked against the entry point with a caller-provided workspace
 (prox_ffn_forward / prox_ffn_forward_residual), bitwise on the output and
 the mask, over calls in a row on one device: the 8B-shape layer, then a
-smaller layer with a residual, then a batch of four, then the first layer
+smaller layer with a residual, then a batch of four, then an int4-proxy
+layer of 16416 channels (its top-k a second launch), then the first layer
 again (the array keeps the previous call's contents; the counters must be
 back at zero for each next call).  The outputs also meet the oracle's
 acceptance rules.  No device memory is taken by the calls once the array is
@@ -21,7 +22,7 @@ from tests.gpu_util import Layer, log, run_and_check, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _pair(L, x_host, keep, sp, residual=None):
+def _pair(L, x_host, keep, sp, residual=None, mode="int8_row"):
     """The no-alloc call and the workspace call on the same inputs; both
     outputs and masks must be bitwise equal.  Returns the change in free
     device memory across a second no-alloc call on the same inputs (the
@@ -32,15 +33,15 @@ def _pair(L, x_host, keep, sp, residual=None):
     res = to_dev(residual) if residual is not None else None
     out_a = torch.empty_like(x)
     sel_a = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
-    P.ffn_forward_noalloc(x, L.w, L.proxy("int8_row"), keep, sp, out_a, sel_out=sel_a, residual=res)
-    ws = P.alloc_workspace(L.d, L.F, B, "int8_row")
+    P.ffn_forward_noalloc(x, L.w, L.proxy(mode), keep, sp, out_a, sel_out=sel_a, residual=res)
+    ws = P.alloc_workspace(L.d, L.F, B, mode)
     sel_b = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
-    out_b = P.ffn_forward(x, L.w, L.proxy("int8_row"), keep, sp, sel_out=sel_b, residual=res, workspace=ws)
+    out_b = P.ffn_forward(x, L.w, L.proxy(mode), keep, sp, sel_out=sel_b, residual=res, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out_a.view(torch.uint8), out_b.view(torch.uint8)), "outputs differ"
     assert torch.equal(sel_a, sel_b), "masks differ"
     free0 = torch.cuda.mem_get_info()[0]
-    P.ffn_forward_noalloc(x, L.w, L.proxy("int8_row"), keep, sp, out_a, sel_out=sel_a, residual=res)
+    P.ffn_forward_noalloc(x, L.w, L.proxy(mode), keep, sp, out_a, sel_out=sel_a, residual=res)
     torch.cuda.synchronize()
     free1 = torch.cuda.mem_get_info()[0]
     assert torch.equal(out_a.view(torch.uint8), out_b.view(torch.uint8)), "outputs differ on the repeat"
@@ -54,12 +55,15 @@ def test_noalloc_matches_workspace_calls():
     x_small = synth.make_x(1, 1024, "bf16", seed=2)
     r_small = synth.make_x(1, 1024, "bf16", seed=3)
     x_b4 = synth.make_x(4, 1024, "bf16", seed=4)
+    wide = Layer(1024, 16416, 0.02, "bf16", seed=5)  # int4 beyond 16384 channels: scores, then the top-k launch
+    x_wide = synth.make_x(1, 1024, "bf16", seed=6)
     d0 = _pair(big, x_big, 0.5, 0.7)                 # first call on the device: the array is set up
     d1 = _pair(small, x_small, 0.5, 0.7, r_small)    # a smaller layer, with a residual
     d2 = _pair(small, x_b4, 0.5, 0.6)                # a batch of four
+    d4 = _pair(wide, x_wide, 0.5, 0.7, mode="int4_g128")
     d3 = _pair(big, x_big, 0.5, 0.7)                 # the first layer again
-    log("free device memory change across repeated no-alloc calls: %d, %d, %d, %d bytes" % (d0, d1, d2, d3))
-    assert d0 == 0 and d1 == 0 and d2 == 0 and d3 == 0
+    log("free device memory change across repeated no-alloc calls: %d, %d, %d, %d, %d bytes" % (d0, d1, d2, d4, d3))
+    assert d0 == 0 and d1 == 0 and d2 == 0 and d4 == 0 and d3 == 0
     # and that result (bitwise the same on both entry points) meets the oracle's acceptance rules
     run_and_check(small, x_small, "int8_row", 0.5, 0.7, residual=r_small, label="small layer with residual")
 
