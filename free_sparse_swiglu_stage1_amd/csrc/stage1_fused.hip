@@ -233,12 +233,16 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
     const uint32_t row_bytes = 2u * (uint32_t)half_bytes;
     for (int t0 = wv; t0 < nk; t0 += kFW * U) {
         uint32_t wg[U], wu[U];
+        // every load issued (clamped), no branches.  Plain loads, not
+        // streaming ones: measured over back-to-back layers, 48.9 against
+        // 49.5 us a layer at 4096 x 14336 (Stage 1 alone 0.3 us slower; the
+        // rows Stage 2 keeps its streaming loads, 1.6 us faster with them)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {  // every load issued (clamped), no branches
+        for (int u = 0; u < U; ++u) {
             const int t = min(t0 + kFW * u, nk - 1);
             const uint32_t o = (uint32_t)sm.li[t] * row_bytes + col_off;
-            wg[u] = __builtin_nontemporal_load((const uint32_t *)(codes + o));
-            wu[u] = __builtin_nontemporal_load((const uint32_t *)(codes + o + (uint32_t)half_bytes));
+            wg[u] = *reinterpret_cast<const uint32_t *>(codes + o);
+            wu[u] = *reinterpret_cast<const uint32_t *>(codes + o + (uint32_t)half_bytes);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
