@@ -229,20 +229,22 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
 #pragma unroll
     for (int n = 0; n < CPL; ++n) acc[0][n] = acc[1][n] = ga[0][n] = ga[1][n] = 0.0f;
     int cur_g = 0;
-    const uint32_t col_off = (uint32_t)cc * QBITS / 8;  // codes are < 4 GiB: 32-bit offsets
+    const uint32_t col_off = (uint32_t)cc * QBITS / 8;  // codes are < 1 GiB here: 32-bit offsets
     const uint32_t row_bytes = 2u * (uint32_t)half_bytes;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(codes), (short)0, (int)(row_bytes * (uint32_t)d), CoherentBuf::kWord3);
     for (int t0 = wv; t0 < nk; t0 += kFW * U) {
         uint32_t wg[U], wu[U];
-        // every load issued (clamped), no branches.  Plain loads, not
-        // streaming ones: measured over back-to-back layers, 48.9 against
-        // 49.5 us a layer at 4096 x 14336 (Stage 1 alone 0.3 us slower; the
-        // rows Stage 2 keeps its streaming loads, 1.6 us faster with them)
+        // every load issued (clamped), no branches: buffer loads on a 32-bit
+        // offset (global loads on 64-bit addresses: Stage 1 1.2 us slower at
+        // 4096 x 14336), with the default cache policy (streaming loads:
+        // 0.9 us a layer slower over back-to-back layers)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = min(t0 + kFW * u, nk - 1);
             const uint32_t o = (uint32_t)sm.li[t] * row_bytes + col_off;
-            wg[u] = *reinterpret_cast<const uint32_t *>(codes + o);
-            wu[u] = *reinterpret_cast<const uint32_t *>(codes + o + (uint32_t)half_bytes);
+            wg[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)o, 0, 0);
+            wu[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)(o + (uint32_t)half_bytes), 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
