@@ -237,14 +237,17 @@ __global__ __launch_bounds__(kFT, 4) void stage1_fused_kernel(const T *__restric
         uint32_t wg[U], wu[U];
         // every load issued (clamped), no branches: buffer loads on a 32-bit
         // offset (global loads on 64-bit addresses: Stage 1 1.2 us slower at
-        // 4096 x 14336), with the default cache policy (streaming loads:
-        // 0.9 us a layer slower over back-to-back layers)
+        // 4096 x 14336), streaming.  The cache policies of the two stages'
+        // streams were chosen together, over back-to-back layers: with the
+        // rows Stage 2's down rows read plainly, streaming codes here give
+        // 47.1-47.3 us a layer at 4096 x 14336 against 47.6-47.8 for the
+        // default policy here and streaming down rows.
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = min(t0 + kFW * u, nk - 1);
             const uint32_t o = (uint32_t)sm.li[t] * row_bytes + col_off;
-            wg[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)o, 0, 0);
-            wu[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)(o + (uint32_t)half_bytes), 0, 0);
+            wg[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)o, 0, 2);
+            wu[u] = __builtin_amdgcn_raw_buffer_load_b32(crs, (int)(o + (uint32_t)half_bytes), 0, 2);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

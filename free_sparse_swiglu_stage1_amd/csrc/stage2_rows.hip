@@ -47,6 +47,7 @@ constexpr int kRT = 1024;         // threads per workgroup
 constexpr int kRW = kRT / 64;     // waves
 constexpr int kRSumGroups = 32;   // partial groups of a slice sum
 constexpr int kRSliceCols = 32;   // columns of a slice
+constexpr int kStream = 2;        // buffer-load cache policy: streaming (non-temporal)
 
 struct RowsArgs {
     const uint16_t *x;         // [d] bf16
@@ -70,18 +71,20 @@ template <typename TW> struct RowPiece;
 template <> struct RowPiece<uint16_t> {
     using V = u32x4;
     static constexpr int N = 8;  // columns
+    template <int AUX>  // cache policy
     static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t off)
     {
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
     }
     static __device__ __forceinline__ void unpack(const V &v, float *f) { vec16<uint16_t>::unpack(v, f); }
 };
 template <> struct RowPiece<uint8_t> {
     using V = u32x4;
     static constexpr int N = 16;
+    template <int AUX>  // cache policy
     static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t off)
     {
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));  // nontemporal
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
     }
     static __device__ __forceinline__ void unpack(const V &v, float *f)
     {
@@ -157,9 +160,14 @@ __device__ void rows_partial(const RowsArgs &a, int v, RowsSmem<H, TW> &sm, cons
             const int i = (rd * RC + c) * H + grp;
             const bool live = i < nc;
             const uint32_t j = (uint32_t)sm.chan[live ? i : 0];
-            vg[c] = RP::load(grs, live ? j * 2u * rowb + coff : goob);
-            vu[c] = RP::load(grs, live ? j * 2u * rowb + rowb + coff : goob);
-            vd[c] = RP::load(drs, live ? j * rowb + coff : doob);
+            // gate and up rows streaming, down rows with the default policy:
+            // over back-to-back layers (with the proxy codes of the fused
+            // Stage 1 streaming) 47.1-47.3 us a layer at 4096 x 14336 against
+            // 47.6-47.8 with every stream's other choice; this stage alone
+            // 23.6 against 24.6-24.9 us
+            vg[c] = RP::template load<kStream>(grs, live ? j * 2u * rowb + coff : goob);
+            vu[c] = RP::template load<kStream>(grs, live ? j * 2u * rowb + rowb + coff : goob);
+            vd[c] = RP::template load<0>(drs, live ? j * rowb + coff : doob);
         }
     };
     auto process = [&](const V(&vg)[RC], const V(&vu)[RC], const V(&vd)[RC], int rd) {
